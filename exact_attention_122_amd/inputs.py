@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for attention workloads.
+
+This module only draws random numbers and converts their storage type. It
+holds none of the attention arithmetic, so both the fp64 CPU oracle (through
+the tests and the benchmark) and the HIP path can consume the same bytes.
+
+Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
+  draw order Q, K, V, then dO (only when a backward pass is needed);
+  each tensor is ``standard_normal(size=(B, H, N, d), dtype=float32)``;
+  for bf16 workloads the fp32 draw is rounded to bfloat16 with
+  round-to-nearest-even on the bit pattern (the same rule as
+  ``torch.Tensor.to(torch.bfloat16)``).
+Layout: contiguous [B, H, N, d], d innermost. bf16 tensors are carried as
+their uint16 bit patterns.
+
+The workloads mirror the pages' long-context self-attention (score matrices
+of tens of millions of entries per head, 'FlashAttention' on josueisai.com,
+section on the matrix that should never be stored).
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Named workloads. Seeds are fixed so every run sees identical bytes.
+WORKLOADS = {
+    "tiny_fp32": dict(B=1, H=1, N=256, d=64, dtype="fp32", causal=False,
+                      backward=False, seed=1221),
+    "fwd_n2048_d64": dict(B=4, H=16, N=2048, d=64, dtype="bf16", causal=False,
+                          backward=False, seed=1222),
+    "fwd_n8192_d128": dict(B=1, H=32, N=8192, d=128, dtype="bf16",
+                           causal=False, backward=False, seed=1223),
+    "causal_fwd_n16384_d128": dict(B=2, H=32, N=16384, d=128, dtype="bf16",
+                                   causal=True, backward=False, seed=1224),
+    "train_n4096_d128": dict(B=2, H=16, N=4096, d=128, dtype="bf16",
+                             causal=False, backward=True, seed=1225),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1
+    r = (b + 0x7FFF + lsb) >> 16
+    out = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Tensor:
+    """A host tensor as the GPU will see it: raw storage plus its dtype."""
+    storage: np.ndarray          # uint16 bits (bf16) or float32 values
+    dtype: str                   # "bf16" | "fp32"
+    sha256: str = field(default="")
+
+    def __post_init__(self):
+        if not self.sha256:
+            self.sha256 = hashlib.sha256(self.storage.tobytes()).hexdigest()
+
+    @property
+    def shape(self):
+        return self.storage.shape
+
+    def to_f32(self) -> np.ndarray:
+        if self.dtype == "bf16":
+            return bf16_bits_to_f32(self.storage)
+        return self.storage.astype(np.float32, copy=False)
+
+    def to_f64(self) -> np.ndarray:
+        """Exact values widened to float64."""
+        return self.to_f32().astype(np.float64)
+
+    def to_torch(self, device="cpu"):
+        import torch
+        if self.dtype == "bf16":
+            t = torch.from_numpy(self.storage.view(np.int16).copy()).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(self.storage.copy())
+        return t.to(device)
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str) -> Tensor:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "bf16":
+        return Tensor(f32_to_bf16_bits(x), "bf16")
+    if dtype == "fp32":
+        return Tensor(x, "fp32")
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def generate(B: int, H: int, N: int, d: int, dtype: str, seed: int,
+             with_grad_output: bool = False) -> dict:
+    """Draw Q, K, V (and dO) of shape [B, H, N, d] from one seeded PCG64."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    out = {"q": _draw(rng, shape, dtype), "k": _draw(rng, shape, dtype),
+           "v": _draw(rng, shape, dtype)}
+    if with_grad_output:
+        out["do"] = _draw(rng, shape, dtype)
+    return out
+
+
+def generate_workload(name: str) -> dict:
+    w = WORKLOADS[name]
+    return generate(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"],
+                    with_grad_output=w["backward"])
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32, the value handed to both sides."""
+    return float(np.float32(1.0 / np.sqrt(np.float64(d))))

@@ -1,0 +1,339 @@
+"""Pins for the fp64 CPU oracle: nothing here compares the oracle with itself.
+
+Each test ties the oracle to something outside it: hand-derived closed forms,
+invariants the mathematics fixes, the blockwise replay of the pages' online
+softmax procedure, PyTorch's float64 CPU attention and autograd, and central
+finite differences.
+"""
+import ast
+import json
+import math
+import operator
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+from oracle import replay as orp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+# ---------------------------------------------------------------- helpers ---
+
+_BIN = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul,
+        ast.Div: operator.truediv}
+
+
+def _eval(expr: str) -> float:
+    """Evaluate a closed form made of numbers, + - * /, unary -, log()."""
+    def ev(n):
+        if isinstance(n, ast.Expression):
+            return ev(n.body)
+        if isinstance(n, ast.Constant) and isinstance(n.value, (int, float)):
+            return float(n.value)
+        if isinstance(n, ast.BinOp) and type(n.op) in _BIN:
+            return _BIN[type(n.op)](ev(n.left), ev(n.right))
+        if isinstance(n, ast.UnaryOp) and isinstance(n.op, ast.USub):
+            return -ev(n.operand)
+        if (isinstance(n, ast.Call) and isinstance(n.func, ast.Name)
+                and n.func.id == "log" and len(n.args) == 1):
+            return math.log(ev(n.args[0]))
+        raise ValueError(f"unsupported expression: {expr!r}")
+    return ev(ast.parse(expr, mode="eval"))
+
+
+def _arr(x):
+    return np.vectorize(_eval, otypes=[np.float64])(np.array(x, dtype=object))
+
+
+def _load_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ------------------------------------------------------ hand-worked cases ---
+
+@pytest.mark.parametrize("case", _load_cases(), ids=lambda c: c["name"])
+def test_hand_worked_forward(case):
+    q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
+    o, lse = oracle.forward_head(q, k, v, _eval(case["scale"]), case["causal"])
+    np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", _load_cases(), ids=lambda c: c["name"])
+def test_hand_worked_backward(case):
+    q, k, v, do = (_arr(case[n]) for n in ("q", "k", "v", "do"))
+    dq, dk, dv = oracle.backward_head(q, k, v, do, _eval(case["scale"]), case["causal"])
+    np.testing.assert_allclose(dq, _arr(case["dq"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, _arr(case["dk"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, _arr(case["dv"]), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------- invariants ---
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probabilities_implied_by_lse_sum_to_one(causal):
+    n, d, scale = 37, 8, 0.3
+    q, k = _rand((n, d), 1), _rand((n, d), 2)
+    _, lse = oracle.forward_head(q, k, _rand((n, 3), 3), scale, causal)
+    s = scale * q @ k.T
+    if causal:
+        s = np.where(np.triu(np.ones((n, n), bool), 1), -np.inf, s)
+    np.testing.assert_allclose(np.exp(s - lse[:, None]).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_that_constant(causal):
+    n, d = 50, 16
+    c = _rand((1, 5), 4)
+    o, _ = oracle.forward_head(_rand((n, d), 5), _rand((n, d), 6), np.repeat(c, n, 0), 0.25, causal)
+    np.testing.assert_allclose(o, np.repeat(c, n, 0), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(causal):
+    n, d, scale = 40, 8, 0.7
+    q = _rand((n, d), 7)
+    krow = _rand((1, d), 8)
+    v = _rand((n, 6), 9)
+    o, lse = oracle.forward_head(q, np.repeat(krow, n, 0), v, scale, causal)
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    mean = np.cumsum(v, 0) / cnt[:, None] if causal else np.repeat(v.mean(0, keepdims=True), n, 0)
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, scale * (q @ krow[0]) + np.log(cnt), rtol=0, atol=1e-12)
+
+
+def test_single_key_returns_v_and_score():
+    q, k, v = _rand((1, 5), 10), _rand((1, 5), 11), _rand((1, 4), 12)
+    o, lse = oracle.forward_head(q, k, v, 0.9)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.9 * q @ k[0], rtol=0, atol=1e-15)
+
+
+def test_causal_first_row_is_first_value_row():
+    n, d = 20, 4
+    q, k, v = _rand((n, d), 13), _rand((n, d), 14), _rand((n, d), 15)
+    o, lse = oracle.forward_head(q, k, v, 0.5, causal=True)
+    np.testing.assert_allclose(o[0], v[0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0], 0.5 * q[0] @ k[0], rtol=0, atol=1e-15)
+
+
+def test_joint_key_value_permutation_invariance():
+    n, d = 33, 8
+    q, k, v = _rand((n, d), 16), _rand((n, d), 17), _rand((n, 5), 18)
+    perm = np.random.default_rng(19).permutation(n)
+    o1, l1 = oracle.forward_head(q, k, v, 0.4)
+    o2, l2 = oracle.forward_head(q, k[perm], v[perm], 0.4)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_moves_lse_only(causal):
+    n, d, scale = 30, 6, 0.45
+    q, k, v = _rand((n, d), 20), _rand((n, d), 21), _rand((n, 4), 22)
+    u = _rand((d,), 23)
+    o1, l1 = oracle.forward_head(q, k, v, scale, causal)
+    o2, l2 = oracle.forward_head(q, k + u, v, scale, causal)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, scale * q @ u, rtol=0, atol=1e-12)
+
+
+def test_causal_row_equals_attention_over_prefix():
+    n, d = 25, 8
+    q, k, v = _rand((n, d), 24), _rand((n, d), 25), _rand((n, 3), 26)
+    o, lse = oracle.forward_head(q, k, v, 0.6, causal=True)
+    for i in (0, 1, 7, 24):
+        oi, li = oracle.forward_head(q[i:i + 1], k[:i + 1], v[:i + 1], 0.6)
+        np.testing.assert_allclose(o[i], oi[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[i], li[0], rtol=0, atol=1e-13)
+
+
+def test_row_subset_matches_full():
+    n, d = 40, 8
+    q, k, v = _rand((n, d), 27), _rand((n, d), 28), _rand((n, 8), 29)
+    rows = np.array([0, 5, 39, 17])
+    for causal in (False, True):
+        o, lse = oracle.forward_head(q, k, v, 0.3, causal)
+        os_, ls_ = oracle.forward_head(q, k, v, 0.3, causal, rows=rows)
+        np.testing.assert_array_equal(os_, o[rows])
+        np.testing.assert_array_equal(ls_, lse[rows])
+
+
+def test_large_scores_do_not_overflow():
+    # scores near 1e3 would overflow exp() without the row max subtracted
+    q = np.array([[1000.0], [-1000.0], [1000.0]])
+    k = np.array([[1.0], [0.999], [-1.0]])
+    v = np.array([[1.0], [2.0], [3.0]])
+    o, lse = oracle.forward_head(q, k, v, 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    # row 0: s = [1000, 999, -1000]; the last key carries weight exp(-2000) = 0
+    p1 = 1.0 / (1.0 + math.exp(-1.0))
+    np.testing.assert_allclose(o[0, 0], p1 * 1 + (1 - p1) * 2, rtol=1e-14)
+    np.testing.assert_allclose(lse[0], 1000 + math.log(1 + math.exp(-1.0)), rtol=1e-14)
+    # row 1: s = [-1000, -999, 1000]: the last key takes all the weight
+    np.testing.assert_allclose(o[1, 0], 3.0, rtol=1e-14)
+    np.testing.assert_allclose(lse[1], 1000.0, rtol=1e-14)
+
+
+def test_fully_masked_row_reading():
+    # A query whose every key is masked (query index -1 under the causal rule)
+    q, k, v = _rand((1, 4), 30), _rand((3, 4), 31), _rand((3, 2), 32)
+    o, lse = oracle.forward_head(q, k, v, 1.0, causal=True, rows=np.array([-1]))
+    assert np.all(o == 0) and lse[0] == -np.inf
+
+
+# -------------------------------------------- blockwise replay (the pages) ---
+
+@pytest.mark.parametrize("block", [1, 3, 7, 16, 64, 100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_softmax_replay_equals_full_softmax(block, causal):
+    n, d = 100, 16
+    q, k, v = _rand((n, d), 33), _rand((n, d), 34), _rand((n, 12), 35)
+    o_full, l_full = oracle.forward_head(q, k, v, 0.25, causal)
+    o_rep, l_rep = orp.online_softmax_attention(q, k, v, 0.25, orp.partition_keys(n, block),
+                                                causal=causal)
+    np.testing.assert_allclose(o_rep, o_full, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l_rep, l_full, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_replay_random_partitions_and_rising_max(seed):
+    rng = np.random.default_rng(100 + seed)
+    n, d = 77, 8
+    q = rng.standard_normal((n, d)) * 4          # peaky rows
+    k = rng.standard_normal((n, d)) * (1 + np.arange(n) / n)[:, None]  # rising max
+    v = rng.standard_normal((n, 5))
+    cuts = np.sort(rng.choice(np.arange(1, n), size=rng.integers(1, 20), replace=False))
+    bounds = np.concatenate([[0], cuts, [n]])
+    blocks = list(zip(bounds[:-1], bounds[1:]))
+    if seed % 2:
+        blocks = blocks[::-1]                     # order does not matter (exact maths)
+    o_full, l_full = oracle.forward_head(q, k, v, 0.5)
+    o_rep, l_rep = orp.online_softmax_attention(q, k, v, 0.5, blocks)
+    np.testing.assert_allclose(o_rep, o_full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l_rep, l_full, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------- independent library special case ---
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_matches_torch_sdpa_float64(causal):
+    b, h, n, d = 2, 3, 45, 16
+    q, k, v = (_rand((b, h, n, d), s) for s in (40, 41, 42))
+    scale = 0.19
+    o, lse = oracle.forward(q, k, v, scale, causal, workers=2)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale,
+                                                           is_causal=causal)
+    s = scale * tq @ tk.transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd_float64(causal):
+    b, h, n, d = 1, 2, 29, 8
+    q, k, v, do = (_rand((b, h, n, d), s) for s in (50, 51, 52, 53))
+    scale = 0.37
+    dq, dk, dv = oracle.backward(q, k, v, do, scale, causal, workers=2)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale,
+                                                           is_causal=causal)
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------- finite differences ---
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_finite_differences(causal):
+    n, d, scale, eps = 6, 3, 0.8, 1e-6
+    q, k, v, do = _rand((n, d), 60), _rand((n, d), 61), _rand((n, d), 62), _rand((n, d), 63)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, scale, causal)
+
+    def loss(qq, kk, vv):
+        return float((oracle.forward_head(qq, kk, vv, scale, causal)[0] * do).sum())
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.abs(num - g).max() / max(1e-12, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+
+
+# ---------------------------------------------------- gradient invariants ---
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(causal):
+    n, d = 31, 8
+    q, k, v, do = _rand((n, d), 70), _rand((n, d), 71), _rand((n, d), 72), _rand((n, d), 73)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, 0.3, causal)
+    # shifting every key by the same vector leaves O unchanged
+    np.testing.assert_allclose(dk.sum(0), 0.0, rtol=0, atol=1e-12)
+    # each probability row sums to one
+    np.testing.assert_allclose(dv.sum(0), do.sum(0), rtol=0, atol=1e-12)
+    # constant V: O does not depend on Q or K
+    dq0, dk0, _ = oracle.backward_head(q, k, np.repeat(v[:1], n, 0), do, 0.3, causal)
+    np.testing.assert_allclose(dq0, 0.0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk0, 0.0, rtol=0, atol=1e-13)
+
+
+def test_batched_equals_per_head():
+    b, h, n, d = 2, 2, 19, 4
+    q, k, v, do = (_rand((b, h, n, d), s) for s in (80, 81, 82, 83))
+    o, lse = oracle.forward(q, k, v, 0.5, True, workers=3)
+    dq, dk, dv = oracle.backward(q, k, v, do, 0.5, True, workers=3)
+    for bi in range(b):
+        for hi in range(h):
+            oh, lh = oracle.forward_head(q[bi, hi], k[bi, hi], v[bi, hi], 0.5, True)
+            gq, gk, gv = oracle.backward_head(q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], 0.5, True)
+            np.testing.assert_array_equal(o[bi, hi], oh)
+            np.testing.assert_array_equal(lse[bi, hi], lh)
+            np.testing.assert_array_equal(dq[bi, hi], gq)
+            np.testing.assert_array_equal(dk[bi, hi], gk)
+            np.testing.assert_array_equal(dv[bi, hi], gv)
+
+
+def test_row_chunking_does_not_change_results(monkeypatch):
+    n, d = 50, 8
+    q, k, v, do = _rand((n, d), 90), _rand((n, d), 91), _rand((n, d), 92), _rand((n, d), 93)
+    o1, l1 = oracle.forward_head(q, k, v, 0.5, True)
+    g1 = oracle.backward_head(q, k, v, do, 0.5, True)
+    monkeypatch.setattr(oa, "_ROW_CHUNK", 7)
+    o2, l2 = oracle.forward_head(q, k, v, 0.5, True)
+    g2 = oracle.backward_head(q, k, v, do, 0.5, True)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_score_matrix_size_at_8k_tokens():
+    # The pages count about 64 million score entries at 8,000 tokens per head;
+    # the long-context workload (8192 tokens) has exactly 2**26 of them.
+    assert 8192 * 8192 == 2 ** 26
+    assert abs(8000 * 8000 - 64e6) < 1
