@@ -1,0 +1,163 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (tiled QK^T, online softmax, PV, O + LSE) followed by fa_bwd (row dot,
+recomputed P, dV, dP, dS, dK, dQ). The default workload is the long-context
+self-attention shape B=1, H=32, N=8192, d=128, bf16, non-causal; its inputs
+(Q, K, V, dO) are resident in HBM before the timed region starts.
+
+FLOPs follow the attention convention: forward 4*N^2*d per head (halved under
+causal masking), backward 2.5x that. Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s (4·N²·d per head) and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def attention_flops(B, H, N, d, causal):
+    f = 4.0 * N * N * d * B * H
+    return f / 2 if causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_n8192_d128")
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads the CPU oracle times")
+    ap.add_argument("--fwd-only", action="store_true", help="time fa_fwd alone (profiling aid)")
+    return ap.parse_args()
+
+
+def cpu_baseline(g, w, scale, causal, heads):
+    """The fp64 oracle on a bounded sample: `heads` whole heads, fwd + bwd."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    q, k, v, do = (g[x].to_f64()[0, :heads] for x in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, scale, causal, workers=cores)
+    oracle.backward(q, k, v, do, scale, causal, workers=cores)
+    dt = time.perf_counter() - t0
+    flops = attention_flops(1, heads, w["N"], w["d"], causal) * 3.5
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{heads} of {w['B'] * w['H']} heads, forward + backward, fp64 numpy "
+                      f"(S materialised row-chunk by row-chunk), same input bytes"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: heads are independent and would shard with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_122_amd import fa, inputs
+
+    w = dict(inputs.WORKLOADS[args.workload])
+    if args.causal is not None:
+        w["causal"] = bool(args.causal)
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    if w["dtype"] != "bf16":
+        raise SystemExit("bench.py times the bf16 path")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scale = inputs.default_scale(d)
+    g = inputs.generate(B, H, N, d, "bf16", w["seed"], with_grad_output=True)
+    q, k, v, do = (g[x].to_torch(dev) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        if not args.fwd_only:
+            fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+            if ev is not None:
+                ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    f_fwd = attention_flops(B, H, N, d, causal)
+    f_bwd = 2.5 * f_fwd
+    res = {}
+    res["fwd"] = {"ms": round(fwd_avg, 4), "tflops": round(f_fwd / fwd_avg / 1e9, 2),
+                  "frac_peak": round(f_fwd / fwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    step_flops = f_fwd
+    if not args.fwd_only:
+        bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        bwd_avg = sum(bwd_ms) / len(bwd_ms)
+        res["bwd"] = {"ms": round(bwd_avg, 4), "tflops": round(f_bwd / bwd_avg / 1e9, 2),
+                      "frac_peak": round(f_bwd / bwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        step_flops += f_bwd
+    value = step_flops / ms_per_step / 1e9   # TFLOP/s
+
+    # roofline of fa_fwd's kernel: algorithmic FLOPs per launch / event-timed launch duration
+    ach = f_fwd / fwd_avg / 1e9
+    roof = {"kernel": f"fwd_bf16_kernel<{d},{'causal' if causal else 'full'}> (fa_fwd)",
+            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_bytes": B * H * (4 * N * d * 2 + N * 4)}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"bf16 self-attention B={B} H={H} N={N} d={d} "
+                               f"{'causal' if causal else 'non-causal'}, step = fa_fwd + fa_bwd"
+                               + (" (fwd only)" if args.fwd_only else ""),
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "seed": w["seed"],
+                   "scale": scale},
+        **res,
+        "frac_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "device": torch.cuda.get_device_name(dev),
+        "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
+    }
+    if not args.no_cpu_baseline and not args.fwd_only:
+        out["cpu_baseline"] = cpu_baseline(g, w, scale, causal, min(args.cpu_heads, B * H))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

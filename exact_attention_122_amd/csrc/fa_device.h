@@ -1,0 +1,163 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Lane layouts used throughout (wave64, checked on gfx950 hardware):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//     B: lane l holds B[8 * (l / 32) + e][l % 32]
+//     D: lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+//   ds_read_b64_tr_b16 (per group of 16 lanes): lane i receives element i % 4
+//     of the 8 bytes addressed by lane 4 * j + i / 4, for j = 0..3.
+//   v_permlane32_swap(x, x): r[1] of lane l < 32 holds x of lane l + 32 and
+//     r[0] of lane l >= 32 holds x of lane l - 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bfloat16 storage in global memory
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// max / sum of x over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even float -> bf16, packed pairwise (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of ROWS x D bf16, row-major, 16-byte chunks XOR-swizzled per row so
+// that the two read patterns below spread over all banks.
+//   * row-operand reads (ds_read_b128): 32 lanes read 32 consecutive rows at
+//     one chunk; swizzling by the row index spreads them over distinct chunks.
+//   * transposed reads (ds_read_b64_tr_b16): a 16-lane group reads 4
+//     consecutive rows x 32 bytes; the row swizzle moves the 4 rows to
+//     distinct chunk pairs.
+// ---------------------------------------------------------------------------
+//   f(row) = 2 * (row % 4) + (row / 4) % 2 (+ 8 * ((row / 8) % 2) with 16
+//   chunks per row): any 8 aligned consecutive rows get 8 distinct f (mod 8),
+//   and any 4 aligned consecutive rows get distinct f / 2, so chunk pairs
+//   {c, c + 1} (c even) land on 8 distinct chunks.
+template <int D>
+struct Swz {
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  __device__ __forceinline__ static int chunk(int row, int c) {
+    const int f = ((row & 3) << 1) | ((row >> 2) & 1);
+    if constexpr (kChunks >= 16) {
+      return c ^ (f | (row & 8));
+    } else {
+      return c ^ f;
+    }
+  }
+  // element offset of (row, col) for a col that is a multiple of 4
+  __device__ __forceinline__ static int offset(int row, int col) {
+    return row * D + (chunk(row, col >> 3) << 3) + (col & 7);
+  }
+};
+
+// A/B operand of 8 consecutive elements of one row, columns [c8*8, c8*8+8).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const bf16_t* tile, int row, int c8) {
+  const FA_LDS bf16x8* p =
+      (const FA_LDS bf16x8*)((const FA_LDS bf16_t*)tile + row * D + (Swz<D>::chunk(row, c8) << 3));
+  return *p;
+}
+
+// Transposed operand: with rows r0 + 4 * half-wave + {0..3} (read 0) and
+// r0 + 8 + 4 * half-wave + {0..3} (read 1), lane l receives column
+// c0 + (l % 32) of those 8 rows, i.e. a 32x16 A operand whose k index runs
+// over rows in the order the score accumulators hold them.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr8(const bf16_t* tile, int r0, int c0, int lane) {
+  const int s = lane & 15;
+  const int hw = lane >> 5;
+  const int col = c0 + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
+  const int row_a = r0 + 4 * hw + (s >> 2);
+  const int row_b = row_a + 8;
+  const FA_LDS bf16_t* base = (const FA_LDS bf16_t*)tile;
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + Swz<D>::offset(row_a, col)));
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + Swz<D>::offset(row_b, col)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Cooperative tile copy global -> registers -> LDS. ROWS x D bf16, rows at
+// or beyond `valid_rows` are filled with zeros.
+template <int ROWS, int D, int THREADS>
+struct TileCopy {
+  static constexpr int kChunks = ROWS * D / 8;
+  static constexpr int kPerThread = kChunks / THREADS;
+  static_assert(kChunks % THREADS == 0, "tile must split evenly over threads");
+  u32x4 r[kPerThread];
+
+  __device__ __forceinline__ void load(const bf16_t* src, int valid_rows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = tid + i * THREADS;
+      const int row = c / (D / 8);
+      const int ch = c % (D / 8);
+      if (row < valid_rows) {
+        r[i] = *(const u32x4*)(src + (size_t)row * D + ch * 8);
+      } else {
+        r[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = tid + i * THREADS;
+      const int row = c / (D / 8);
+      const int ch = c % (D / 8);
+      *(FA_LDS u32x4*)((FA_LDS bf16_t*)tile + row * D + (Swz<D>::chunk(row, ch) << 3)) = r[i];
+    }
+  }
+};
+
+// Work-group id remap so that consecutive logical blocks (the query blocks of
+// one head) run on the same XCD and share its L2: hardware hands work-group
+// ids to the 8 XCDs round-robin.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  if ((nblocks & 7) != 0) return bid;
+  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+}  // namespace fa

@@ -1,0 +1,163 @@
+"""Thin Python binding of libfa.so (ctypes), same names as include/fa.h.
+
+Only argument marshalling lives here: tensors become device pointers, the
+current torch stream becomes the hipStream_t, and a non-OK status becomes a
+RuntimeError carrying the library's detail message. Every step of the
+attention computation runs in the library's HIP kernels; if the library is
+missing this module raises instead of computing anything another way.
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_BF16 = 0
+FA_FP32 = 1
+
+EXPORTS = ("fa_version", "fa_status_string", "fa_last_error_detail", "fa_fwd",
+           "fa_bwd_workspace_bytes", "fa_bwd")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -m exact_attention_122_amd.build` "
+            "(or __graft_entry__.build()); there is no other implementation to fall back on")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_version.restype = i
+    lib.fa_version.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_last_error_detail.restype = ctypes.c_char_p
+    lib.fa_last_error_detail.argtypes = []
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------ raw C calls ---
+
+def fa_version() -> int:
+    return load_library().fa_version()
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_last_error_detail() -> str:
+    return load_library().fa_last_error_detail().decode()
+
+
+def _check(status: int, what: str):
+    if status != FA_OK:
+        raise RuntimeError(f"{what} failed: {fa_status_string(status)}: {fa_last_error_detail()}")
+
+
+# --------------------------------------------------------- torch helpers ---
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise RuntimeError(f"dtype {t.dtype} is not built (bfloat16 or float32)")
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise RuntimeError(f"expected [B, H, N, d] tensors, got shape {tuple(q.shape)}")
+    return tuple(int(x) for x in q.shape)
+
+
+def _same(ref, *ts):
+    for t in ts:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise RuntimeError("all [B, H, N, d] tensors must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise RuntimeError("tensors must be contiguous [B, H, N, d]")
+    if not ref.is_cuda:
+        raise RuntimeError("tensors must live in GPU memory")
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32 (the value the C call receives)."""
+    return float(ctypes.c_float(1.0 / math.sqrt(d)).value)
+
+
+def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention forward of [B, H, N, d] tensors (see include/fa.h)."""
+    import torch
+    _same(q, k, v)
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _same(q, out)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise RuntimeError("lse must be a contiguous float32 [B, H, N] tensor")
+    st = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                               _dtype_code(q), _stream(q))
+    _check(st, "fa_fwd")
+    return out, lse
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype: int = FA_BF16) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d, dtype))
+
+
+def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+           dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of sum(O * dO) for O = fa_fwd(q, k, v) (see include/fa.h)."""
+    import torch
+    _same(q, k, v, o, do)
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = default_scale(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _same(q, dq, dk, dv)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise RuntimeError("lse must be a contiguous float32 [B, H, N] tensor")
+    st = load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
+                               workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,117 @@
+/*
+ * fa.h - C ABI of the exact-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention the way the
+ * 'FlashAttention' pages describe it: Q, K and V are cut into tiles that live
+ * on chip, the score tile S = scale * Q K^T is formed block by block, a running
+ * row maximum and row sum fold each block into the output (online softmax,
+ * josueisai.com section on the softmax trick; 'log-sum-exp' rescaling on the
+ * kerneldigest.dev glossary entry), and only O plus one log-sum-exp per row
+ * reach memory. The backward pass keeps no score or probability matrix: it
+ * recomputes them from Q, K, V and the saved log-sum-exp (josueisai.com
+ * section on recomputing instead of remembering).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are dense, contiguous [B, H, N, d] with d innermost. Q, K, V, O,
+ *    dO, dQ, dK and dV all have the element type `dtype`; LSE is always
+ *    float32 [B, H, N] and holds the natural-log log-sum-exp of the scaled
+ *    scores of each query row.
+ *  - Every tensor pointer is a DEVICE pointer (memory of the current HIP
+ *    device). Base pointers must be 16-byte aligned. The caller allocates and
+ *    owns every buffer; the library allocates, frees and retains nothing.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; outputs are valid once the stream reaches that point and
+ *    inputs must stay unchanged until then.
+ *  - causal = 1 masks key j for query i whenever j > i (top-left alignment,
+ *    equal query and key lengths). Tiles that are wholly masked are skipped.
+ *  - B, H or N equal to 0 is an empty problem: nothing is enqueued and FA_OK
+ *    is returned.
+ *  - Errors are returned as fa_status; no exception crosses the ABI. A
+ *    request the kernels do not cover returns FA_ERR_UNSUPPORTED; there is
+ *    never a silent fallback to a different implementation. After an error,
+ *    fa_last_error_detail() (thread-local) explains it.
+ *  - The functions are thread-safe and keep no state between calls.
+ */
+#ifndef EXACT_ATTENTION_FA_H
+#define EXACT_ATTENTION_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad flag ... */
+  FA_ERR_UNSUPPORTED = 2,      /* valid request outside what is built */
+  FA_ERR_HIP = 3               /* HIP runtime or launch failure */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_BF16 = 0, /* bfloat16 storage, float32 accumulation */
+  FA_FP32 = 1  /* float32 storage and arithmetic (no reduced-precision modes) */
+} fa_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(int status);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* fa_last_error_detail(void);
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and
+ * LSE_i = ln sum_j exp(scale * q_i . k_j) over the unmasked keys j.
+ * (josueisai.com 'FlashAttention': three-step definition in the section on the
+ * matrix that should never be stored; tiling and the running max / running sum
+ * in the section on the softmax trick.)
+ *
+ *  Q, K, V  in   [B, H, N, d] of `dtype`
+ *  O        out  [B, H, N, d] of `dtype` (rounded to nearest even from fp32)
+ *  LSE      out  [B, H, N] float32
+ *  scale    any finite float (1/sqrt(d) in the usual use)
+ *  d        64 or 128
+ *  dtype    FA_BF16 or FA_FP32
+ * O and LSE must not overlap any input.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem: one float32 per
+ * query row (the row dot product D_i = sum_k dO_ik O_ik), rounded up to 256.
+ * Returns 0 for an empty problem or for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass: the gradients of sum(O * dO) with respect to Q, K and V,
+ * where O = fa_fwd(Q, K, V). Scores and probabilities are recomputed from Q,
+ * K and the saved LSE (josueisai.com 'FlashAttention', section on recomputing
+ * instead of remembering); with P = exp(scale S - LSE):
+ *   dV = P^T dO;  dP = dO V^T;  D_i = sum_k dO_ik O_ik;
+ *   dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
+ * LSE is an input only (it is not differentiated).
+ *
+ *  Q, K, V, O, dO  in   [B, H, N, d] of `dtype`; O and LSE as fa_fwd wrote them
+ *  LSE             in   [B, H, N] float32
+ *  dQ, dK, dV      out  [B, H, N, d] of `dtype`
+ *  workspace       device scratch of at least fa_bwd_workspace_bytes() bytes,
+ *                  16-byte aligned, owned by the caller
+ *  d               64 or 128;  dtype FA_BF16 only (FA_FP32 -> UNSUPPORTED)
+ * Outputs and the workspace must not overlap any input or each other.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* EXACT_ATTENTION_FA_H */

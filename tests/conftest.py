@@ -26,3 +26,10 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # name the case before any GPU work starts, so a run that dies still says where
+    if "gpu" in nodeid:
+        sys.__stderr__.write(f"[start] {nodeid}\n")
+        sys.__stderr__.flush()

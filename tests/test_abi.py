@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects bad requests on the host before any HIP
+call (no kernel is launched from these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_122_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+# fake, 16-byte aligned, never dereferenced: validation fails before any use
+P = [0x10000 * (i + 1) for i in range(12)]
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\**\s+\**(fa_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_bound_functions():
+    assert declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert fa.fa_version() >= 100
+    assert fa.fa_status_string(fa.FA_OK) == "FA_OK"
+    assert fa.fa_status_string(fa.FA_ERR_INVALID_ARGUMENT) == "FA_ERR_INVALID_ARGUMENT"
+    assert fa.fa_status_string(fa.FA_ERR_UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(fa.FA_ERR_HIP) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def fwd(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=128, d=64, scale=0.125,
+        causal=0, dtype=fa.FA_BF16):
+    lib = fa.load_library()
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def bwd(*, ptrs=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16,
+        ws=P[9], ws_bytes=1 << 20):
+    lib = fa.load_library()
+    ptrs = ptrs or P[:9]
+    return lib.fa_bwd(*ptrs, B, H, N, d, scale, causal, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARGUMENT, "Q is NULL"),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARGUMENT, "LSE is NULL"),
+    (dict(v=P[2] + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
+    (dict(d=0), fa.FA_ERR_INVALID_ARGUMENT, "positive"),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(o=P[0]), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(lse=P[1] + 64), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_INVALID_ARGUMENT, "INT_MAX"),
+])
+def test_fwd_rejects_on_the_host(kw, status, needle):
+    assert fwd(**kw) == status
+    assert needle in fa.fa_last_error_detail()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_fwd_empty_problem_is_a_no_op(kw):
+    assert fwd(**kw) == fa.FA_OK
+    assert fa.fa_last_error_detail() == ""
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARGUMENT, "smaller"),
+    (dict(ptrs=[P[0]] + P[1:6] + [P[1]] + P[7:9]), fa.FA_ERR_INVALID_ARGUMENT, "dQ overlaps K"),
+    (dict(ptrs=P[:7] + [P[6]] + P[8:9]), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(ws=P[8]), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARGUMENT, "causal"),
+])
+def test_bwd_rejects_on_the_host(kw, status, needle):
+    assert bwd(**kw) == status
+    assert needle in fa.fa_last_error_detail()
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    assert bwd(N=0, ptrs=[0] * 9, ws=0, ws_bytes=0) == fa.FA_OK
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP32) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="GPU memory"):
+        fa.fa_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load_library.__wrapped__(str(tmp_path / "nope.so")) if hasattr(fa.load_library, "__wrapped__") \
+            else _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = fa._lib
+    fa._lib = None
+    try:
+        return fa.load_library(path)
+    finally:
+        fa._lib = saved

@@ -1,0 +1,123 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times. The oracle checks sampled query rows one by one (each row
+sees its whole key row), whole heads for the backward, and properties that hold
+for every row."""
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_122_amd import fa, inputs
+
+from gpu_util import REL_FRO, TOL, compare, f64, gpu_fwd, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(n, rng, count=192):
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1]
+    rows = np.concatenate([np.array([r for r in edge if 0 <= r < n]), rng.integers(0, n, size=count)])
+    return np.unique(rows)
+
+
+def _check_sampled_forward(name, g, o, lse, heads, scale, causal):
+    w = inputs.WORKLOADS[name]
+    rng = np.random.default_rng(w["seed"])
+    dtype = w["dtype"]
+    o64, l64 = f64(o), f64(lse)
+    q, k, v = g["q"].storage, g["k"].storage, g["v"].storage
+    tensor = lambda s: inputs.Tensor(s, dtype)
+    for flat in heads:
+        b, h = divmod(flat, w["H"])
+        rows = _sample_rows(w["N"], rng)
+        ro, rl = oracle.forward_head(tensor(q[b, h]).to_f64(), tensor(k[b, h]).to_f64(),
+                                     tensor(v[b, h]).to_f64(), scale, causal, rows=rows)
+        compare(f"O[{b},{h}]", o64[b, h, rows], ro, TOL[dtype]["o"], REL_FRO if dtype == "bf16" else None)
+        compare(f"LSE[{b},{h}]", l64[b, h, rows], rl, TOL[dtype]["lse"])
+    # every row: finite, and LSE close to ln(#keys) + 1/2 for N(0,1) scores
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(l64))
+    n = w["N"]
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    dev = np.abs(l64 - (np.log(cnt) + 0.5)).mean(axis=-1)
+    assert np.all(dev < 0.5), dev.max()
+
+
+def test_tiny_fp32_full():
+    name = "tiny_fp32"
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    scale = inputs.default_scale(w["d"])
+    _, _, _, o, lse = gpu_fwd(g, w["causal"], scale)
+    ro, rl = oracle.forward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), scale, w["causal"])
+    compare("O", f64(o), ro, TOL["fp32"]["o"])
+    compare("LSE", f64(lse), rl, TOL["fp32"]["lse"])
+
+
+def test_fwd_n2048_d64_full():
+    name = "fwd_n2048_d64"
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    scale = inputs.default_scale(w["d"])
+    _, _, _, o, lse = gpu_fwd(g, w["causal"], scale)
+    ro, rl = oracle.forward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), scale, w["causal"])
+    compare("O", f64(o), ro, TOL["bf16"]["o"], REL_FRO)
+    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
+
+
+def test_fwd_n8192_d128_sampled():
+    name = "fwd_n8192_d128"
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    scale = inputs.default_scale(w["d"])
+    _, _, _, o, lse = gpu_fwd(g, w["causal"], scale)
+    _check_sampled_forward(name, g, o, lse, heads=[0, 13, 31], scale=scale, causal=False)
+
+
+def test_causal_fwd_n16384_d128_sampled():
+    name = "causal_fwd_n16384_d128"
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    scale = inputs.default_scale(w["d"])
+    _, _, _, o, lse = gpu_fwd(g, True, scale)
+    _check_sampled_forward(name, g, o, lse, heads=[0, 37, 63], scale=scale, causal=True)
+
+
+def test_train_n4096_d128_fwd_and_bwd():
+    name = "train_n4096_d128"
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    scale = inputs.default_scale(w["d"])
+    q, k, v, o, lse = gpu_fwd(g, False, scale)
+    _check_sampled_forward(name, g, o, lse, heads=[0, 21], scale=scale, causal=False)
+    do = to_dev(g["do"])
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=scale)
+    torch.cuda.synchronize()
+    gq, gk, gv = f64(dq), f64(dk), f64(dv)
+    for flat in (0, 17, 31):
+        b, h = divmod(flat, w["H"])
+        rq, rk, rv = oracle.backward_head(g["q"].to_f64()[b, h], g["k"].to_f64()[b, h], g["v"].to_f64()[b, h],
+                                          g["do"].to_f64()[b, h], scale, False)
+        compare(f"dQ[{b},{h}]", gq[b, h], rq, TOL["bf16"]["grad"], REL_FRO)
+        compare(f"dK[{b},{h}]", gk[b, h], rk, TOL["bf16"]["grad"], REL_FRO)
+        compare(f"dV[{b},{h}]", gv[b, h], rv, TOL["bf16"]["grad"], REL_FRO)
+    # properties of every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    assert np.abs(gk.sum(axis=2)).max() < 0.25
+    np.testing.assert_allclose(gv.sum(axis=2), g["do"].to_f64().sum(axis=2), rtol=0, atol=0.25)
+
+
+def test_causal_bwd_n16384_d128_heads():
+    """Causal backward at the long causal shape, whole heads checked."""
+    name = "causal_fwd_n16384_d128"
+    w = inputs.WORKLOADS[name]
+    n, d = w["N"], w["d"]
+    g = inputs.generate(1, 2, n, d, "bf16", seed=w["seed"] + 100, with_grad_output=True)
+    scale = inputs.default_scale(d)
+    q, k, v, o, lse = gpu_fwd(g, True, scale)
+    do = to_dev(g["do"])
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_head(g["q"].to_f64()[0, 1], g["k"].to_f64()[0, 1], g["v"].to_f64()[0, 1],
+                                      g["do"].to_f64()[0, 1], scale, True)
+    compare("dQ", f64(dq)[0, 1], rq, TOL["bf16"]["grad"], REL_FRO)
+    compare("dK", f64(dk)[0, 1], rk, TOL["bf16"]["grad"], REL_FRO)
+    compare("dV", f64(dv)[0, 1], rv, TOL["bf16"]["grad"], REL_FRO)
