@@ -42,7 +42,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads the CPU oracle times")
     ap.add_argument("--fwd-only", action="store_true", help="time fa_fwd alone (profiling aid)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (read + write) instead, to scale "
+                         "hardware byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain elementwise copy kernel of known size: reads and writes mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy (torch.neg) of float32", "launches": 3,
+                      "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}), flush=True)
 
 
 def cpu_baseline(g, w, scale, causal, heads):
@@ -64,6 +81,9 @@ def cpu_baseline(g, w, scale, causal, heads):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path: heads are independent and would shard with no exchange.", file=sys.stderr)

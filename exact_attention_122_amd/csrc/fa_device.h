@@ -119,6 +119,50 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16_t* tile, int r0, int c0, in
   return __builtin_bit_cast(bf16x8, z);
 }
 
+// Per-lane byte offsets of the two LDS read patterns, computed once per kernel
+// so the reads in the loop need no address arithmetic (tile base and constant
+// row offsets fold into the instruction's immediate offset).
+//  RowRead: A/B operand of 8 consecutive elements of row (lane % 32) + 32 kb,
+//           columns [16 ks + 8 hw, +8).
+//  TrRead:  the transposed operand of lds_tr8 at rows 16 t, columns 32 db.
+template <int D>
+struct RowRead {
+  uint32_t off[D / 16];
+  __device__ __forceinline__ void init(int lane) {
+    const int row = lane & 31, hw = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(row * D + (Swz<D>::chunk(row, 2 * ks + hw) << 3)) * 2;
+  }
+  __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int kb, int ks) const {
+    return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks] + kb * 32 * D * 2);
+  }
+};
+
+template <int D>
+struct TrRead {
+  uint32_t off[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int s = lane & 15, hw = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 4 * hw + (s >> 2) + 8 * i;
+        const int col = 32 * db + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
+        off[db][i] = (uint32_t)Swz<D>::offset(row, col) * 2;
+      }
+  }
+  // rows t * 16 + ... (f(row) only depends on row % 16, so +16 rows is a constant)
+  __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int t, int db) const {
+    const FA_LDS char* base = (const FA_LDS char*)(const FA_LDS bf16_t*)tile + t * 16 * D * 2;
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][0]));
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][1]));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(bf16x8, z);
+  }
+};
+
 // Cooperative tile copy global -> registers -> LDS. ROWS x D bf16, rows at
 // or beyond `valid_rows` are filled with zeros.
 template <int ROWS, int D, int THREADS>
@@ -151,6 +195,53 @@ struct TileCopy {
     }
   }
 };
+
+// Direct global -> LDS tile copy (buffer_load ... lds, 16 bytes per lane).
+// A ROWS x D bf16 tile is THREADS/64 waves x kInstr instructions; instruction
+// i of wave w fills LDS bytes [(w * kInstr + i) * 1024, +1024) of the tile, lane
+// l writing 16 bytes at +16 l. Each lane therefore fetches the global chunk
+// that the swizzled layout stores at its LDS position. Rows past the end of
+// the buffer resource (num_records) arrive as zeros, so ragged tails need no
+// branches. No registers hold the tile.
+template <int ROWS, int D, int THREADS>
+struct TileDma {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = ROWS * kRowBytes;
+  static constexpr int kWaves = THREADS / 64;
+  static constexpr int kInstr = kTileBytes / 1024 / kWaves;
+  static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into whole 1 KB wave copies");
+  uint32_t lane_off[kInstr];  // byte offset of this lane's chunk inside a global tile
+  int lds_off;                // byte offset of this wave's first 1 KB inside an LDS tile
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    lds_off = wave * kInstr * 1024;
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int pos = lds_off + i * 1024 + 16 * lane;  // LDS byte position in the tile
+      const int row = pos / kRowBytes;
+      const int chunk = (pos % kRowBytes) / 16;
+      lane_off[i] = (uint32_t)(row * kRowBytes + Swz<D>::chunk(row, chunk) * 16);
+    }
+  }
+  // Copy rows [row0, row0 + ROWS) of the tensor behind `rsrc` into `tile`.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0) const {
+    const uint32_t base = (uint32_t)row0 * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      FA_LDS void* dst = (FA_LDS void*)((FA_LDS char*)(FA_LDS bf16_t*)tile + lds_off + i * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, base + lane_off[i], 0, 0, 0);
+    }
+  }
+};
+
+// Buffer resource over `bytes` bytes at `base`; loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wait until every vector-memory operation of this wave (including the
+// direct-to-LDS copies) has completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Work-group id remap so that consecutive logical blocks (the query blocks of
 // one head) run on the same XCD and share its L2: hardware hands work-group

@@ -51,84 +51,112 @@ struct FwdParams {
   uint32_t qsign;  // 0x80008000 flips two bf16 signs at once when scale < 0
 };
 
-template <int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const bf16_t* kt, const bf16_t* vt, const bf16x8 (&qf)[D / 16],
+// One 64-key tile for this wave's 32 query rows. `masked` tiles (causal
+// diagonal, ragged end) set the scores of dead keys to -inf first.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile(const bf16_t* kt, const bf16_t* vt, const RowRead<D>& krd,
+                                         const TrRead<D>& vrd, const bf16x8 (&qf)[D / 16],
                                          f32x16 (&acc)[D / 32], float& m, float& l, float& mc,
-                                         const FwdParams& p, int key0, int qi, int lane) {
+                                         const FwdParams& p, int key0, int qi, int lane, bool masked) {
   const int hw = lane >> 5;
-  const int col = lane & 31;
 
   // S^T for keys [key0, key0 + 64) x this wave's 32 queries
   f32x16 s0 = {}, s1 = {};
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 a0 = lds_row8<D>(kt, col, 2 * ks + hw);
-    const bf16x8 a1 = lds_row8<D>(kt, col + 32, 2 * ks + hw);
-    s0 = mfma32(a0, qf[ks], s0);
-    s1 = mfma32(a1, qf[ks], s1);
+    s0 = mfma32(krd(kt, 0, ks), qf[ks], s0);
+    s1 = mfma32(krd(kt, 1, ks), qf[ks], s1);
   }
-  float sv[32];
+  if (masked) {
+    // key of register r of block b: key0 + 32 b + 8 (r / 4) + 4 hw + r % 4
+    const int lim = CAUSAL ? min(qi, p.n - 1) : p.n - 1;  // last live key of this row
+    const int k0 = key0 + 4 * hw;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    sv[i] = s0[i];
-    sv[16 + i] = s1[i];
-  }
-  if constexpr (MASKED) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int key = key0 + (i >> 4) * 32 + 8 * ((i & 15) >> 2) + 4 * hw + (i & 3);
-      const bool dead = key >= p.n || (CAUSAL && key > qi);
-      sv[i] = dead ? -INFINITY : sv[i];
+    for (int r = 0; r < 16; ++r) {
+      const int kr = k0 + 8 * (r >> 2) + (r & 3);
+      s0[r] = kr > lim ? -INFINITY : s0[r];
+      s1[r] = kr + 32 > lim ? -INFINITY : s1[r];
     }
   }
   // running max: in-lane over 32 keys, then across the half-wave pair
-  float mx = sv[0];
+  float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-  for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sv[i]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
   mx = pair_max(mx);
 
-  const bool need = !(mx <= m + p.thr);
-  if (wave_any(need)) {
+  if (wave_any(!(mx <= m + p.thr))) {
     const float mnew = fmaxf(m, mx);
     const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c;
     const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m * p.c - ms);
     l *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
     m = mnew;
     mc = ms;
   }
 
-  float rs = 0.f;
+  // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0
+  const float nmc = -mc;
+  float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float e = fast_exp2(fmaf(sv[i], p.c, -mc));
-    if constexpr (MASKED) e = (sv[i] == -INFINITY) ? 0.f : e;
-    sv[i] = e;
-    rs += e;
+  for (int r = 0; r < 16; ++r) {
+    const float e0 = fast_exp2(fmaf(s0[r], p.c, nmc));
+    const float e1 = fast_exp2(fmaf(s1[r], p.c, nmc));
+    s0[r] = e0;
+    s1[r] = e1;
+    rs0 += e0;
+    rs1 += e1;
   }
-  l += rs;
+  l += rs0 + rs1;
 
   bf16x8 pb[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) pb[t] = pack_bf16x8(&sv[(t >> 1) * 16 + 8 * (t & 1)]);
-
+  for (int e = 0; e < 8; ++e) {
+    pb[0][e] = (__bf16)s0[e];
+    pb[1][e] = (__bf16)s0[8 + e];
+    pb[2][e] = (__bf16)s1[e];
+    pb[3][e] = (__bf16)s1[8 + e];
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[db] = mfma32(lds_tr8<D>(vt, 16 * t, 32 * db, lane), pb[t], acc[db]);
+    for (int t = 0; t < 4; ++t) acc[db] = mfma32(vrd(vt, t, db), pb[t], acc[db]);
+}
+
+// Tile j: start copying tile j + 1 into the other buffers, compute tile j,
+// then wait for the copy and publish it to the whole work-group.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_step(int j, int n_tiles, const bf16_t* kt, const bf16_t* vt, bf16_t* kn,
+                                         bf16_t* vn, const TileDma<kBlockN, D, kThreads>& dma,
+                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                         const RowRead<D>& krd, const TrRead<D>& vrd, const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&acc)[D / 32], float& m, float& l, float& mc, const FwdParams& p,
+                                         int qi, int wq0, int w_last, bool wave_has_rows, int lane) {
+  const int key0 = j * kBlockN;
+  if (j + 1 < n_tiles) {
+    dma.issue(krs, kn, key0 + kBlockN);
+    dma.issue(vrs, vn, key0 + kBlockN);
+  }
+  if (wave_has_rows && (!CAUSAL || key0 <= w_last)) {
+    const bool masked = (key0 + kBlockN > p.n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
+    fwd_tile<D, CAUSAL>(kt, vt, krd, vrd, qf, acc, m, l, mc, p, key0, qi, lane, masked);
+  }
+  wait_vmem();
+  __syncthreads();
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][kBlockN * D];
-  __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][kBlockN * D];
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+  // Two K and two V tiles, declared as separate objects so the compiler can
+  // see that reading one tile never depends on the copy filling the other.
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kBlockN * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kBlockN * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kBlockN * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kBlockN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = lane >> 5;
   const int col = lane & 31;
   const int n = p.n;
@@ -142,18 +170,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int wq0 = q_row0 + wave * 32;
   const int qi = wq0 + col;
 
+  // K/V tiles stream straight into LDS; start the first one before loading Q
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)n * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)n * D * 2);
+  TileDma<kBlockN, D, kThreads> dma;
+  dma.init(wave, lane);
+  RowRead<D> krd;
+  krd.init(lane);
+  TrRead<D> vrd;
+  vrd.init(lane);
+  dma.issue(krs, k_lds0, 0);
+  dma.issue(vrs, v_lds0, 0);
+
   bf16x8 qf[D / 16];
   {
     const bf16_t* qrow = p.q + head_off + (size_t)qi * D + 8 * hw;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (qi < n) x = *(const uint4*)(qrow + 16 * ks);
-      x.x ^= p.qsign;
-      x.y ^= p.qsign;
-      x.z ^= p.qsign;
-      x.w ^= p.qsign;
-      qf[ks] = __builtin_bit_cast(bf16x8, x);
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (qi < n) x = *(const u32x4*)(qrow + 16 * ks);
+      qf[ks] = __builtin_bit_cast(bf16x8, x ^ p.qsign);
     }
   }
 
@@ -167,36 +203,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f, mc = 0.f;
 
-  const bf16_t* kbase = p.k + head_off;
-  const bf16_t* vbase = p.v + head_off;
-  TileCopy<kBlockN, D, kThreads> kc, vc;
-  kc.load(kbase, n, tid);
-  vc.load(vbase, n, tid);
-  kc.store(k_lds[0], tid);
-  vc.store(v_lds[0], tid);
+  wait_vmem();
   __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const int key0 = j * kBlockN;
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      kc.load(kbase + (size_t)(key0 + kBlockN) * D, n - key0 - kBlockN, tid);
-      vc.load(vbase + (size_t)(key0 + kBlockN) * D, n - key0 - kBlockN, tid);
-    }
-    const bool active = wave_has_rows && (!CAUSAL || key0 <= w_last);
-    if (active) {
-      const bool masked = (key0 + kBlockN > n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
-      if (masked)
-        fwd_tile<D, CAUSAL, true>(k_lds[buf], v_lds[buf], qf, acc, m, l, mc, p, key0, qi, lane);
-      else
-        fwd_tile<D, CAUSAL, false>(k_lds[buf], v_lds[buf], qf, acc, m, l, mc, p, key0, qi, lane);
-    }
-    if (more) {
-      kc.store(k_lds[buf ^ 1], tid);
-      vc.store(v_lds[buf ^ 1], tid);
-    }
-    __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    fwd_step<D, CAUSAL>(j, n_tiles, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, acc, m, l, mc, p,
+                        qi, wq0, w_last, wave_has_rows, lane);
+    if (j + 1 < n_tiles)
+      fwd_step<D, CAUSAL>(j + 1, n_tiles, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, acc, m, l,
+                          mc, p, qi, wq0, w_last, wave_has_rows, lane);
   }
 
   // epilogue: O = acc / l, LSE = m * |scale| + ln l
@@ -217,6 +231,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+template __global__ void fwd_bf16_kernel<64, false>(FwdParams);
+template __global__ void fwd_bf16_kernel<64, true>(FwdParams);
+template __global__ void fwd_bf16_kernel<128, false>(FwdParams);
+template __global__ void fwd_bf16_kernel<128, true>(FwdParams);
+
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   FwdParams p;
@@ -229,8 +248,11 @@ hipError_t launch(const FwdArgs& a) {
   p.nqb = (a.n + kBlockM - 1) / kBlockM;
   p.nblocks = p.nqb * a.bh;
   p.scale_abs = fabsf(a.scale);
-  p.c = p.scale_abs * kLog2e;
-  p.thr = p.c > 0.f ? 8.f / p.c : 3.0e38f;
+  // c is kept strictly positive: with scale = 0 every exp2(c (s - m)) still
+  // rounds to exactly 1 (uniform weights) while exp2(c * -inf) stays 0 for
+  // masked keys. LSE uses |scale| itself.
+  p.c = fmaxf(p.scale_abs * kLog2e, 1e-30f);
+  p.thr = p.scale_abs > 0.f ? 8.f / p.c : 3.0e38f;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.nblocks), dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
