@@ -56,6 +56,9 @@ int check_shape(int B, int H, int N, int d, int dtype, Problem* pr) {
   // grids use 64-row blocks at the finest: B*H*ceil(N/64) work-groups must fit in int
   if (bh * ((N + 63LL) / 64) > INT_MAX)
     return fail(FA_ERR_INVALID_ARGUMENT, "problem needs more than INT_MAX work-groups");
+  // the bf16 kernels address one head through 32-bit buffer offsets
+  if (dtype == FA_BF16 && (long long)N * d * 2 > INT_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "N*d=%lld: one head exceeds 2 GiB", (long long)N * d);
   pr->bh = bh;
   pr->elems = rows * d;
   pr->tensor_bytes = (size_t)pr->elems * (dtype == FA_BF16 ? 2 : 4);
@@ -124,7 +127,7 @@ FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   Problem pr;
   if (check_shape(B, H, N, d, dtype, &pr) != FA_OK || dtype != FA_BF16 || pr.empty) return 0;
-  return (pr.lse_bytes + 255) / 256 * 256;
+  return fa::bwd_workspace_bytes(pr.bh, N);
 }
 
 FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,

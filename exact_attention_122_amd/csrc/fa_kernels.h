@@ -32,7 +32,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* row_dot;  // workspace: bh * n floats
+  float* workspace;  // bwd_workspace_bytes(bh, n) bytes: per-row statistics
   int bh;
   int n;
   int d;
@@ -44,5 +44,7 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
+// Workspace of fa_bwd: two floats per query row, rows padded to 64 per head.
+size_t bwd_workspace_bytes(long long bh, int n);
 
 }  // namespace fa

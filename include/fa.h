@@ -82,8 +82,9 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this problem: one float32 per
- * query row (the row dot product D_i = sum_k dO_ik O_ik), rounded up to 256.
+ * Bytes of device workspace fa_bwd needs for this problem: two float32 per
+ * query row (the row dot product D_i = sum_k dO_ik O_ik and LSE_i in base 2),
+ * with each head's rows padded to a multiple of 64: B*H*ceil(N/64)*64*8.
  * Returns 0 for an empty problem or for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);

@@ -73,6 +73,7 @@ def bwd(*, ptrs=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, dtype=fa.FA_
     (dict(o=P[0]), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(lse=P[1] + 64), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_INVALID_ARGUMENT, "INT_MAX"),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED, "2 GiB"),
 ])
 def test_fwd_rejects_on_the_host(kw, status, needle):
     assert fwd(**kw) == status
@@ -105,8 +106,9 @@ def test_bwd_empty_problem_is_a_no_op():
 
 
 def test_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 64 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 3, 65, 64) == 3 * 128 * 8
     assert fa.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP32) == 0
