@@ -13,8 +13,10 @@ causal masking), backward 2.5x that. Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +27,35 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s (4·N²·d per head) and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
+
+
+# HBM bytes per launch of the forward kernel, from the FETCH_SIZE / WRITE_SIZE
+# counter passes summarised in this file (scaled by a copy of known size). The
+# figure is only reported while the kernel's sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_n8192_d128_hbm_bytes.md")
+FWD_SOURCES = ("fa_device.h", "fa_fwd_bf16.hip", "fa_kernels.h")
+
+
+def fwd_source_sha256():
+    h = hashlib.sha256()
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_122_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Counter-derived HBM bytes per launch of `kernel`, or None if not measured
+    for the current sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel=(\S+) read_bytes=(\d+) write_bytes=(\d+) traffic_bytes=(\d+) "
+                  r"source_sha256=([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel or m.group(5) != fwd_source_sha256():
+        return None
+    return int(m.group(4))
 
 
 def attention_flops(B, H, N, d, causal):
@@ -40,7 +71,7 @@ def parse():
     ap.add_argument("--workload", default="fwd_n8192_d128")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads the CPU oracle times")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads the CPU oracle times")
     ap.add_argument("--fwd-only", action="store_true", help="time fa_fwd alone (profiling aid)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (read + write) instead, to scale "
@@ -154,9 +185,10 @@ def main():
 
     # roofline of fa_fwd's kernel: algorithmic FLOPs per launch / event-timed launch duration
     ach = f_fwd / fwd_avg / 1e9
-    roof = {"kernel": f"fwd_bf16_kernel<{d},{'causal' if causal else 'full'}> (fa_fwd)",
+    kname = f"fwd_bf16_kernel<{d},{'causal' if causal else 'full'}>"
+    roof = {"kernel": f"{kname} (fa_fwd)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),
             "algorithmic_bytes": B * H * (4 * N * d * 2 + N * 4)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
