@@ -30,6 +30,9 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN-quieting before max/min: every NaN the kernels could see comes
+    # from NaN inputs, whose outputs are meaningless either way
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,
 ]

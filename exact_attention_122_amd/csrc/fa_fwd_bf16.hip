@@ -9,8 +9,18 @@
 // chip.
 //
 // Mapping to the hardware:
-//  * 4 waves x 32 query rows per work-group; K/V tiles of 64 keys,
-//    double-buffered in LDS, one barrier per tile.
+//  * 8 waves x 32 query rows per work-group, one work-group per CU at d = 128
+//    (two at d = 64), so every SIMD runs one wave of group A (waves 0-3) next
+//    to one of group B (waves 4-7).
+//  * Ping-pong: each tile's work splits into a matrix phase (O += P_{j-1} V_{j-1}
+//    for the previous tile, then S_j = K_j Q^T) and a softmax phase (max, exp,
+//    sum of S_j). Group B runs one phase behind group A and a work-group
+//    barrier separates phases, so on every SIMD one wave feeds the matrix core
+//    while the other runs the softmax on the vector ALU.
+//  * Both groups use K_j and V_{j-1} during iteration j, so the two tiles are
+//    loaded together as one set, double-buffered in LDS; group A copies set
+//    j+1 global -> LDS (buffer_load ... lds, zero-fill past the end) while set
+//    j is in use.
 //  * Scores are computed transposed, S^T = K Q^T, with Q (the B operand) kept
 //    in registers. Each lane then holds one query's scores for 32 keys, so the
 //    row max and row sum are in-lane reductions plus one exchange across the
@@ -31,7 +41,7 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per work-group
 constexpr int kBlockN = 64;           // keys per tile
@@ -51,22 +61,82 @@ struct FwdParams {
   uint32_t qsign;  // 0x80008000 flips two bf16 signs at once when scale < 0
 };
 
-// One 64-key tile for this wave's 32 query rows. `masked` tiles (causal
-// diagonal, ragged end) set the scores of dead keys to -inf first.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(const bf16_t* kt, const bf16_t* vt, const RowRead<D>& krd,
-                                         const TrRead<D>& vrd, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&acc)[D / 32], float& m, float& l, float& mc,
-                                         const FwdParams& p, int key0, int qi, int lane, bool masked) {
-  const int hw = lane >> 5;
+// Per-wave running state of 32 query rows (one per lane pair l, l ^ 32).
+template <int D>
+struct RowState {
+  f32x16 acc[D / 32];  // O^T: register r of acc[db] holds d = 32 db + 8 (r / 4) + 4 hw + r % 4
+  f32x16 s0, s1;       // S^T of the current tile (keys 0-31 and 32-63)
+  bf16x8 pb[4];        // P of the previous tile as bf16 B operands
+  float m, l, mc;
+};
 
-  // S^T for keys [key0, key0 + 64) x this wave's 32 queries
+// Scheduling groups (see __builtin_amdgcn_sched_group_barrier): instruction
+// classes the compiler's scheduler must place in the given order.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Pins a value's computation before this point: the empty asm claims to
+// read and rewrite the registers, so the compiler cannot sink the code that
+// produces them past a later barrier into the next phase (which would undo the
+// ping-pong between the two wave groups).
+template <typename T>
+__device__ __forceinline__ void fence_regs(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// O += P_{j-1} V_{j-1}
+template <int D>
+__device__ __forceinline__ void pv_mfma(RowState<D>& st, const bf16_t* vt, const TrRead<D>& vrd) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) st.acc[db] = mfma32(vrd(vt, t, db), st.pb[t], st.acc[db]);
+}
+
+// Matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.
+// The 48 LDS operand reads run ahead of the 32 MFMAs: at every MFMA about
+// four operands are already in flight, so the matrix core does not wait on
+// LDS latency (the other wave on the SIMD is in its softmax phase and cannot
+// cover it).
+template <int D>
+__device__ __forceinline__ void matrix_phase(RowState<D>& st, const bf16_t* kt, const bf16_t* vt,
+                                             const RowRead<D>& krd, const TrRead<D>& vrd,
+                                             const bf16x8 (&qf)[D / 16]) {
+  pv_mfma<D>(st, vt, vrd);
   f32x16 s0 = {}, s1 = {};
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     s0 = mfma32(krd(kt, 0, ks), qf[ks], s0);
     s1 = mfma32(krd(kt, 1, ks), qf[ks], s1);
   }
+  st.s0 = s0;
+  st.s1 = s1;
+  fence_regs(st.s0);
+  fence_regs(st.s1);
+  // PV: D / 8 MFMAs, two transposed reads each; S: D / 8 MFMAs, one read each
+  constexpr int kPv = D / 8, kS = D / 8, kAhead = 4;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < kPv - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+}
+
+// Softmax phase for the tile whose scores are in st.s0 / st.s1. `masked` tiles
+// (causal diagonal, ragged end) set the scores of dead keys to -inf first.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& p, int key0, int qi, int lane,
+                                              bool masked) {
+  const int hw = lane >> 5;
+  f32x16 s0 = st.s0, s1 = st.s1;
   if (masked) {
     // key of register r of block b: key0 + 32 b + 8 (r / 4) + 4 hw + r % 4
     const int lim = CAUSAL ? min(qi, p.n - 1) : p.n - 1;  // last live key of this row
@@ -84,19 +154,19 @@ __device__ __forceinline__ void fwd_tile(const bf16_t* kt, const bf16_t* vt, con
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
   mx = pair_max(mx);
 
-  if (wave_any(!(mx <= m + p.thr))) {
-    const float mnew = fmaxf(m, mx);
+  if (wave_any(!(mx <= st.m + p.thr))) {
+    const float mnew = fmaxf(st.m, mx);
     const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c;
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m * p.c - ms);
-    l *= alpha;
+    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m * p.c - ms);
+    st.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    m = mnew;
-    mc = ms;
+    for (int db = 0; db < D / 32; ++db) st.acc[db] *= alpha;
+    st.m = mnew;
+    st.mc = ms;
   }
 
   // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0
-  const float nmc = -mc;
+  const float nmc = -st.mc;
   float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -107,48 +177,58 @@ __device__ __forceinline__ void fwd_tile(const bf16_t* kt, const bf16_t* vt, con
     rs0 += e0;
     rs1 += e1;
   }
-  l += rs0 + rs1;
-
-  bf16x8 pb[4];
+  st.l += rs0 + rs1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    pb[0][e] = (__bf16)s0[e];
-    pb[1][e] = (__bf16)s0[8 + e];
-    pb[2][e] = (__bf16)s1[e];
-    pb[3][e] = (__bf16)s1[8 + e];
+    st.pb[0][e] = (__bf16)s0[e];
+    st.pb[1][e] = (__bf16)s0[8 + e];
+    st.pb[2][e] = (__bf16)s1[e];
+    st.pb[3][e] = (__bf16)s1[8 + e];
   }
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[db] = mfma32(vrd(vt, t, db), pb[t], acc[db]);
+  for (int t = 0; t < 4; ++t) fence_regs(st.pb[t]);
+  fence_regs(st.l);
 }
 
-// Tile j: start copying tile j + 1 into the other buffers, compute tile j,
-// then wait for the copy and publish it to the whole work-group.
+// One iteration j < n_tiles of the main loop: group A copies set j + 1
+// (K_{j+1} into `kn`, V_j into `vn`), then matrix(j) on set j (K_j in `kt`,
+// V_{j-1} in `vt`), a barrier, softmax(j), the wait for this wave's copies and
+// a barrier. The buffers are fixed per call (the loop is unrolled by two) so
+// the compiler can see that reading set j never depends on the copy into the
+// other set. Every wave runs every tile of its work-group: a tile wholly past
+// a wave's last causal key has all scores at -inf, so its p are 0 and it
+// changes nothing.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_step(int j, int n_tiles, const bf16_t* kt, const bf16_t* vt, bf16_t* kn,
-                                         bf16_t* vn, const TileDma<kBlockN, D, kThreads>& dma,
-                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         const RowRead<D>& krd, const TrRead<D>& vrd, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&acc)[D / 32], float& m, float& l, float& mc, const FwdParams& p,
-                                         int qi, int wq0, int w_last, bool wave_has_rows, int lane) {
+__device__ __forceinline__ void fwd_iteration(int j, int n_tiles, bool group_b, const bf16_t* kt, const bf16_t* vt,
+                                              bf16_t* kn, bf16_t* vn, const TileDma<kBlockN, D, kThreads / 2>& dma,
+                                              __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                              const RowRead<D>& krd, const TrRead<D>& vrd,
+                                              const bf16x8 (&qf)[D / 16], RowState<D>& st, const FwdParams& p,
+                                              int wq0, int qi, int lane) {
+  if (!group_b) {
+    if (j + 1 < n_tiles) dma.issue(krs, kn, (j + 1) * kBlockN);
+    dma.issue(vrs, vn, j * kBlockN);
+  }
+  matrix_phase<D>(st, kt, vt, krd, vrd, qf);
+  __syncthreads();
   const int key0 = j * kBlockN;
-  if (j + 1 < n_tiles) {
-    dma.issue(krs, kn, key0 + kBlockN);
-    dma.issue(vrs, vn, key0 + kBlockN);
-  }
-  if (wave_has_rows && (!CAUSAL || key0 <= w_last)) {
-    const bool masked = (key0 + kBlockN > p.n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
-    fwd_tile<D, CAUSAL>(kt, vt, krd, vrd, qf, acc, m, l, mc, p, key0, qi, lane, masked);
-  }
+  const bool masked = (key0 + kBlockN > p.n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
+  softmax_phase<D, CAUSAL>(st, p, key0, qi, lane, masked);
   wait_vmem();
   __syncthreads();
 }
 
+// d = 64 needs few enough registers (at most 128 per lane) for two
+// work-groups per CU; d = 128 runs one.
+template <int D>
+constexpr int fwd_blocks_per_cu() {
+  return D <= 64 ? 2 : 1;
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  // Two K and two V tiles, declared as separate objects so the compiler can
-  // see that reading one tile never depends on the copy filling the other.
+__global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_kernel(FwdParams p) {
+  // Two sets of (K tile, V tile), declared as separate objects so the compiler
+  // can see that reading one set never depends on the copy filling the other.
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kBlockN * D];
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kBlockN * D];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kBlockN * D];
@@ -157,6 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_b = wave >= kWaves / 2;
   const int hw = lane >> 5;
   const int col = lane & 31;
   const int n = p.n;
@@ -170,17 +251,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int wq0 = q_row0 + wave * 32;
   const int qi = wq0 + col;
 
-  // K/V tiles stream straight into LDS; start the first one before loading Q
+  // K/V tiles stream straight into LDS. Group A copies every tile (see the
+  // loop below); start the first K tile before loading Q.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)n * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)n * D * 2);
-  TileDma<kBlockN, D, kThreads> dma;
-  dma.init(wave, lane);
+  TileDma<kBlockN, D, kThreads / 2> dma;
+  dma.init(wave & (kWaves / 2 - 1), lane);
   RowRead<D> krd;
   krd.init(lane);
   TrRead<D> vrd;
   vrd.init(lane);
-  dma.issue(krs, k_lds0, 0);
-  dma.issue(vrs, v_lds0, 0);
+  if (!group_b) dma.issue(krs, k_lds0, 0);
 
   bf16x8 qf[D / 16];
   {
@@ -195,26 +276,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int q_last = min(n, q_row0 + kBlockM) - 1;
   const int n_tiles = CAUSAL ? (q_last / kBlockN + 1) : (n + kBlockN - 1) / kBlockN;
-  const int w_last = min(n - 1, wq0 + 31);
-  const bool wave_has_rows = wq0 < n;
 
-  f32x16 acc[D / 32];
+  RowState<D> st;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f, mc = 0.f;
+  for (int db = 0; db < D / 32; ++db) st.acc[db] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.pb[t] = bf16x8{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.mc = 0.f;
+  // the first matrix phase multiplies P = 0 by the V buffer of set 0: zero it
+  for (int i = tid; i < kBlockN * D / 8; i += kThreads) ((FA_LDS u32x4*)(FA_LDS bf16_t*)v_lds0)[i] = u32x4{};
 
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
-    fwd_step<D, CAUSAL>(j, n_tiles, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, acc, m, l, mc, p,
-                        qi, wq0, w_last, wave_has_rows, lane);
-    if (j + 1 < n_tiles)
-      fwd_step<D, CAUSAL>(j + 1, n_tiles, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, acc, m, l,
-                          mc, p, qi, wq0, w_last, wave_has_rows, lane);
+  // Iteration j uses LDS set j % 2 = {K_j, V_{j-1}}: matrix(j) = O += P_{j-1}
+  // V_{j-1} and S_j = K_j Q^T, then softmax(j). Both groups run this same
+  // loop, group B one phase (one barrier) behind group A, so while one group
+  // is in its matrix phase the other is in its softmax phase. Group A copies
+  // set j + 1 during its iteration j (phases 2j and 2j + 1); set j is last
+  // read by group B in phase 2j + 1, and set j + 1 is first read by group A in
+  // phase 2j + 2.
+  if (group_b) __syncthreads();
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    fwd_iteration<D, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
+                             wq0, qi, lane);
+    fwd_iteration<D, CAUSAL>(j + 1, n_tiles, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, st,
+                             p, wq0, qi, lane);
   }
+  if (j < n_tiles)
+    fwd_iteration<D, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
+                             wq0, qi, lane);
+  // last tile: O += P V of set n_tiles (no copy is in flight any more)
+  pv_mfma<D>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
+  if (!group_b) __syncthreads();
 
   // epilogue: O = acc / l, LSE = m * |scale| + ln l
-  const float lt = pair_sum(l);
+  const float lt = pair_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n) {
     bf16_t* orow = p.o + head_off + (size_t)qi * D;
@@ -223,11 +322,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 w;
-        w.x = pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
-        w.y = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        w.x = pack_bf16x2(st.acc[db][4 * g] * inv, st.acc[db][4 * g + 1] * inv);
+        w.y = pack_bf16x2(st.acc[db][4 * g + 2] * inv, st.acc[db][4 * g + 3] * inv);
         *(uint2*)(orow + db * 32 + 8 * g + 4 * hw) = w;
       }
-    if (hw == 0) p.lse[(size_t)head * n + qi] = lt > 0.f ? m * p.scale_abs + __logf(lt) : -INFINITY;
+    if (hw == 0) p.lse[(size_t)head * n + qi] = lt > 0.f ? st.m * p.scale_abs + __logf(lt) : -INFINITY;
   }
 }
 
