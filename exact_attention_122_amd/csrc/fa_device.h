@@ -65,26 +65,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles of ROWS x D bf16, row-major, 16-byte chunks XOR-swizzled per row so
-// that the two read patterns below spread over all banks.
-//   * row-operand reads (ds_read_b128): 32 lanes read 32 consecutive rows at
-//     one chunk; swizzling by the row index spreads them over distinct chunks.
-//   * transposed reads (ds_read_b64_tr_b16): a 16-lane group reads 4
-//     consecutive rows x 32 bytes; the row swizzle moves the 4 rows to
-//     distinct chunk pairs.
+// that both read patterns below are free of bank conflicts. gfx950's LDS has
+// 64 banks of 4 bytes, so one cycle serves 16 slots of 16 bytes; slot =
+// (row * D / 8 + physical chunk) mod 16.
+//   * row-operand reads (ds_read_b128): 16 lanes per cycle read 16
+//     consecutive rows at one logical chunk c; they need 16 distinct slots.
+//   * transposed reads (ds_read_b64_tr_b16): 32 lanes per cycle read 4
+//     consecutive rows (aligned to 4) x 4 consecutive chunks (aligned to 4);
+//     they need 16 distinct slots.
+// physical chunk = c ^ f(row), with f depending on row % 16:
+//   D = 128 (16 chunks, slot = chunk): f = 4 (row % 4) + (row / 4) % 4 is a
+//     permutation of 0..15 (row reads), and 4 aligned rows get distinct
+//     f / 4, i.e. distinct aligned groups of 4 chunks (transposed reads).
+//   D = 64 (8 chunks, slot = 8 (row % 2) + chunk): f = 4 ((row / 2) % 2) +
+//     (row / 4) % 4 is a permutation of 0..7 over the even rows and over the
+//     odd rows of any 16, and rows r, r + 2 of an aligned group of 4 get
+//     distinct f / 4.
 // ---------------------------------------------------------------------------
-//   f(row) = 2 * (row % 4) + (row / 4) % 2 (+ 8 * ((row / 8) % 2) with 16
-//   chunks per row): any 8 aligned consecutive rows get 8 distinct f (mod 8),
-//   and any 4 aligned consecutive rows get distinct f / 2, so chunk pairs
-//   {c, c + 1} (c even) land on 8 distinct chunks.
 template <int D>
 struct Swz {
   static constexpr int kChunks = D / 8;  // 16-byte chunks per row
   __device__ __forceinline__ static int chunk(int row, int c) {
-    const int f = ((row & 3) << 1) | ((row >> 2) & 1);
     if constexpr (kChunks >= 16) {
-      return c ^ (f | (row & 8));
+      return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
     } else {
-      return c ^ f;
+      return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
     }
   }
   // element offset of (row, col) for a col that is a multiple of 4
