@@ -148,10 +148,24 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& 
       s1[r] = kr + 32 > lim ? -INFINITY : s1[r];
     }
   }
-  // running max: in-lane over 32 keys, then across the half-wave pair
-  float mx = fmaxf(s0[0], s1[0]);
+  // Running max: in-lane over 32 keys as a tree (depth 4 instead of a chain
+  // of 16), then across the half-wave pair. The softmax wave has its SIMD's
+  // vector ALU to itself during this phase, so only independent instructions
+  // hide each other's latency.
+  float mx;
+  {
+    float t[11];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
+    t[10] = fmaxf(s0[15], s1[15]);
+    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
+    const float u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+    const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]);
+    const float u3 = fmaxf(t[9], t[10]);
+    mx = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+  }
   mx = pair_max(mx);
 
   if (wave_any(!(mx <= st.m + p.thr))) {
@@ -165,19 +179,32 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& 
     st.mc = ms;
   }
 
-  // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0
+  // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0.
+  // All 32 FMAs, then all 32 exponentials, then a sum tree: independent
+  // instructions back to back instead of FMA -> exp -> add chains.
   const float nmc = -st.mc;
-  float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float e0 = fast_exp2(fmaf(s0[r], p.c, nmc));
-    const float e1 = fast_exp2(fmaf(s1[r], p.c, nmc));
-    s0[r] = e0;
-    s1[r] = e1;
-    rs0 += e0;
-    rs1 += e1;
+    s0[r] = fmaf(s0[r], p.c, nmc);
+    s1[r] = fmaf(s1[r], p.c, nmc);
   }
-  st.l += rs0 + rs1;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = fast_exp2(s0[r]);
+    s1[r] = fast_exp2(s1[r]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = s0[r] + s1[r];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) t[r] += t[r + w];
+    st.l += t[0];
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     st.pb[0][e] = (__bf16)s0[e];
