@@ -11,7 +11,9 @@
 // Mapping to the hardware:
 //  * 8 waves x 32 query rows per work-group, one work-group per CU at d = 128
 //    (two at d = 64), so every SIMD runs one wave of group A (waves 0-3) next
-//    to one of group B (waves 4-7).
+//    to one of group B (waves 4-7). K/V tiles hold 128 keys at d = 128 (64 at
+//    d = 64): long phases amortise the two barriers per tile and give the
+//    softmax more independent work.
 //  * Ping-pong: each tile's work splits into a matrix phase (O += P_{j-1} V_{j-1}
 //    for the previous tile, then S_j = K_j Q^T) and a softmax phase (max, exp,
 //    sum of S_j). Group B runs one phase behind group A and a work-group
@@ -44,7 +46,12 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per work-group
-constexpr int kBlockN = 64;           // keys per tile
+
+// 32-key blocks per K/V tile
+template <int D>
+constexpr int key_blocks() {
+  return D >= 128 ? 4 : 2;
+}
 
 struct FwdParams {
   const bf16_t* q;
@@ -62,11 +69,11 @@ struct FwdParams {
 };
 
 // Per-wave running state of 32 query rows (one per lane pair l, l ^ 32).
-template <int D>
+template <int D, int KB>
 struct RowState {
   f32x16 acc[D / 32];  // O^T: register r of acc[db] holds d = 32 db + 8 (r / 4) + 4 hw + r % 4
-  f32x16 s0, s1;       // S^T of the current tile (keys 0-31 and 32-63)
-  bf16x8 pb[4];        // P of the previous tile as bf16 B operands
+  f32x16 s[KB];        // S^T of the current tile: register r of s[b] holds key 32 b + 8 (r / 4) + 4 hw + r % 4
+  bf16x8 pb[2 * KB];   // P of the previous tile as bf16 B operands (pb[2 b + h] = s[b][8 h .. 8 h + 7])
   float m, l, mc;
 };
 
@@ -85,36 +92,39 @@ __device__ __forceinline__ void fence_regs(T& x) {
 }
 
 // O += P_{j-1} V_{j-1}
-template <int D>
-__device__ __forceinline__ void pv_mfma(RowState<D>& st, const bf16_t* vt, const TrRead<D>& vrd) {
+template <int D, int KB>
+__device__ __forceinline__ void pv_mfma(RowState<D, KB>& st, const bf16_t* vt, const TrRead<D>& vrd) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) st.acc[db] = mfma32(vrd(vt, t, db), st.pb[t], st.acc[db]);
+    for (int t = 0; t < 2 * KB; ++t) st.acc[db] = mfma32(vrd(vt, t, db), st.pb[t], st.acc[db]);
 }
 
 // Matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.
-// The 48 LDS operand reads run ahead of the 32 MFMAs: at every MFMA about
-// four operands are already in flight, so the matrix core does not wait on
-// LDS latency (the other wave on the SIMD is in its softmax phase and cannot
+// The LDS operand reads run ahead of the MFMAs: at every MFMA about four
+// operands are already in flight, so the matrix core does not wait on LDS
+// latency (the other wave on the SIMD is in its softmax phase and cannot
 // cover it).
-template <int D>
-__device__ __forceinline__ void matrix_phase(RowState<D>& st, const bf16_t* kt, const bf16_t* vt,
+template <int D, int KB>
+__device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* kt, const bf16_t* vt,
                                              const RowRead<D>& krd, const TrRead<D>& vrd,
                                              const bf16x8 (&qf)[D / 16]) {
-  pv_mfma<D>(st, vt, vrd);
-  f32x16 s0 = {}, s1 = {};
+  pv_mfma<D, KB>(st, vt, vrd);
+  f32x16 s[KB];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    s0 = mfma32(krd(kt, 0, ks), qf[ks], s0);
-    s1 = mfma32(krd(kt, 1, ks), qf[ks], s1);
+  for (int b = 0; b < KB; ++b) s[b] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int b = 0; b < KB; ++b) s[b] = mfma32(krd(kt, b, ks), qf[ks], s[b]);
+#pragma unroll
+  for (int b = 0; b < KB; ++b) {
+    st.s[b] = s[b];
+    fence_regs(st.s[b]);
   }
-  st.s0 = s0;
-  st.s1 = s1;
-  fence_regs(st.s0);
-  fence_regs(st.s1);
-  // PV: D / 8 MFMAs, two transposed reads each; S: D / 8 MFMAs, one read each
-  constexpr int kPv = D / 8, kS = D / 8, kAhead = 4;
+  // PV: (D / 32) (2 KB) MFMAs, two transposed reads each; S: KB (D / 16)
+  // MFMAs, one read each
+  constexpr int kPv = D * KB / 16, kS = KB * D / 16, kAhead = 4;
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAhead, 0);
 #pragma unroll
   for (int i = 0; i < kPv - kAhead; ++i) {
@@ -130,41 +140,41 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, const bf16_t* kt, 
   for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
 }
 
-// Softmax phase for the tile whose scores are in st.s0 / st.s1. `masked` tiles
+// Softmax phase for the tile whose scores are in st.s. `masked` tiles
 // (causal diagonal, ragged end) set the scores of dead keys to -inf first.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& p, int key0, int qi, int lane,
+template <int D, int KB, bool CAUSAL>
+__device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
                                               bool masked) {
+  constexpr int kN = 16 * KB;  // scores per lane
   const int hw = lane >> 5;
-  f32x16 s0 = st.s0, s1 = st.s1;
+  float x[kN];
+#pragma unroll
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[16 * b + r] = st.s[b][r];
   if (masked) {
-    // key of register r of block b: key0 + 32 b + 8 (r / 4) + 4 hw + r % 4
     const int lim = CAUSAL ? min(qi, p.n - 1) : p.n - 1;  // last live key of this row
     const int k0 = key0 + 4 * hw;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = k0 + 8 * (r >> 2) + (r & 3);
-      s0[r] = kr > lim ? -INFINITY : s0[r];
-      s1[r] = kr + 32 > lim ? -INFINITY : s1[r];
+    for (int i = 0; i < kN; ++i) {
+      const int b = i >> 4, r = i & 15;
+      const int kr = k0 + 32 * b + 8 * (r >> 2) + (r & 3);
+      x[i] = kr > lim ? -INFINITY : x[i];
     }
   }
-  // Running max: in-lane over 32 keys as a tree (depth 4 instead of a chain
-  // of 16), then across the half-wave pair. The softmax wave has its SIMD's
-  // vector ALU to itself during this phase, so only independent instructions
-  // hide each other's latency.
+  // Running max: in-lane as a tree, then across the half-wave pair. The
+  // softmax wave has its SIMD's vector ALU to itself during this phase, so
+  // only independent instructions hide each other's latency.
   float mx;
   {
-    float t[11];
+    float t[kN / 2];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+    for (int i = 0; i < kN / 2; ++i) t[i] = fmaxf(x[i], x[i + kN / 2]);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) t[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
-    t[10] = fmaxf(s0[15], s1[15]);
-    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
-    const float u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
-    const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]);
-    const float u3 = fmaxf(t[9], t[10]);
-    mx = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+    for (int w = kN / 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+    mx = t[0];
   }
   mx = pair_max(mx);
 
@@ -180,40 +190,31 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& 
   }
 
   // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0.
-  // All 32 FMAs, then all 32 exponentials, then a sum tree: independent
-  // instructions back to back instead of FMA -> exp -> add chains.
+  // FMAs, then exponentials, then a sum tree: independent instructions back
+  // to back instead of FMA -> exp -> add chains.
   const float nmc = -st.mc;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = fmaf(s0[r], p.c, nmc);
-    s1[r] = fmaf(s1[r], p.c, nmc);
-  }
+  for (int i = 0; i < kN; ++i) x[i] = fmaf(x[i], p.c, nmc);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = fast_exp2(s0[r]);
-    s1[r] = fast_exp2(s1[r]);
-  }
+  for (int i = 0; i < kN; ++i) x[i] = fast_exp2(x[i]);
   __builtin_amdgcn_sched_barrier(0);
   {
-    float t[16];
+    float t[kN / 2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] = s0[r] + s1[r];
+    for (int i = 0; i < kN / 2; ++i) t[i] = x[i] + x[i + kN / 2];
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
+    for (int w = kN / 4; w >= 1; w >>= 1)
 #pragma unroll
-      for (int r = 0; r < w; ++r) t[r] += t[r + w];
+      for (int i = 0; i < w; ++i) t[i] += t[i + w];
     st.l += t[0];
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    st.pb[0][e] = (__bf16)s0[e];
-    st.pb[1][e] = (__bf16)s0[8 + e];
-    st.pb[2][e] = (__bf16)s1[e];
-    st.pb[3][e] = (__bf16)s1[8 + e];
-  }
+  for (int t = 0; t < 2 * KB; ++t)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) fence_regs(st.pb[t]);
+    for (int e = 0; e < 8; ++e) st.pb[t][e] = (__bf16)x[8 * t + e];
+#pragma unroll
+  for (int t = 0; t < 2 * KB; ++t) fence_regs(st.pb[t]);
   fence_regs(st.l);
 }
 
@@ -225,22 +226,24 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, const FwdParams& 
 // other set. Every wave runs every tile of its work-group: a tile wholly past
 // a wave's last causal key has all scores at -inf, so its p are 0 and it
 // changes nothing.
-template <int D, bool CAUSAL>
+template <int D, int KB, bool CAUSAL>
 __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, bool group_b, const bf16_t* kt, const bf16_t* vt,
-                                              bf16_t* kn, bf16_t* vn, const TileDma<kBlockN, D, kThreads / 2>& dma,
+                                              bf16_t* kn, bf16_t* vn,
+                                              const TileDma<32 * KB, D, kThreads / 2>& dma,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const RowRead<D>& krd, const TrRead<D>& vrd,
-                                              const bf16x8 (&qf)[D / 16], RowState<D>& st, const FwdParams& p,
+                                              const bf16x8 (&qf)[D / 16], RowState<D, KB>& st, const FwdParams& p,
                                               int wq0, int qi, int lane) {
+  constexpr int kBlockN = 32 * KB;
   if (!group_b) {
     if (j + 1 < n_tiles) dma.issue(krs, kn, (j + 1) * kBlockN);
     dma.issue(vrs, vn, j * kBlockN);
   }
-  matrix_phase<D>(st, kt, vt, krd, vrd, qf);
+  matrix_phase<D, KB>(st, kt, vt, krd, vrd, qf);
   __syncthreads();
   const int key0 = j * kBlockN;
   const bool masked = (key0 + kBlockN > p.n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
-  softmax_phase<D, CAUSAL>(st, p, key0, qi, lane, masked);
+  softmax_phase<D, KB, CAUSAL>(st, p, key0, qi, lane, masked);
   wait_vmem();
   __syncthreads();
 }
@@ -254,13 +257,14 @@ constexpr int fwd_blocks_per_cu() {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int KB = key_blocks<D>();
+  constexpr int kBlockN = 32 * KB;  // keys per tile
   // Two sets of (K tile, V tile), declared as separate objects so the compiler
   // can see that reading one set never depends on the copy filling the other.
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kBlockN * D];
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kBlockN * D];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kBlockN * D];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kBlockN * D];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,11 +308,11 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_ker
   const int q_last = min(n, q_row0 + kBlockM) - 1;
   const int n_tiles = CAUSAL ? (q_last / kBlockN + 1) : (n + kBlockN - 1) / kBlockN;
 
-  RowState<D> st;
+  RowState<D, KB> st;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.acc[db] = f32x16{};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) st.pb[t] = bf16x8{};
+  for (int t = 0; t < 2 * KB; ++t) st.pb[t] = bf16x8{};
   st.m = -INFINITY;
   st.l = 0.f;
   st.mc = 0.f;
@@ -327,16 +331,16 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_ker
   if (group_b) __syncthreads();
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
-    fwd_iteration<D, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
+    fwd_iteration<D, KB, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
                              wq0, qi, lane);
-    fwd_iteration<D, CAUSAL>(j + 1, n_tiles, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, st,
+    fwd_iteration<D, KB, CAUSAL>(j + 1, n_tiles, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, st,
                              p, wq0, qi, lane);
   }
   if (j < n_tiles)
-    fwd_iteration<D, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
+    fwd_iteration<D, KB, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
                              wq0, qi, lane);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
-  pv_mfma<D>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
+  pv_mfma<D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) __syncthreads();
 
   // epilogue: O = acc / l, LSE = m * |scale| + ln l
