@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--workload", default="fwd_n8192_d128")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=12, help="heads the CPU oracle times")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads the CPU oracle times (at most B*H)")
     ap.add_argument("--fwd-only", action="store_true", help="time fa_fwd alone (profiling aid)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (read + write) instead, to scale "
