@@ -44,6 +44,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Pins a value at this point of the program: the empty asm claims to read and
+// rewrite the registers, so the compiler can neither sink the code that
+// produces them past a later barrier nor hoist the code that uses them above
+// an earlier one. The kernels use it to keep matrix and vector phases on
+// their side of a work-group barrier.
+template <typename T>
+__device__ __forceinline__ void fence_regs(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }

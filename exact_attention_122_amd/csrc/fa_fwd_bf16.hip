@@ -82,15 +82,6 @@ struct RowState {
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// Pins a value's computation before this point: the empty asm claims to
-// read and rewrite the registers, so the compiler cannot sink the code that
-// produces them past a later barrier into the next phase (which would undo the
-// ping-pong between the two wave groups).
-template <typename T>
-__device__ __forceinline__ void fence_regs(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
 // O += P_{j-1} V_{j-1}
 template <int D, int KB>
 __device__ __forceinline__ void pv_mfma(RowState<D, KB>& st, const bf16_t* vt, const TrRead<D>& vrd) {
