@@ -13,7 +13,18 @@ or reordered beyond what the definition states:
                                     O = PV. The scale factor is an argument
                                     (the pages omit it; every workload passes
                                     1/sqrt(d) rounded to float32).
-  causal: S_ij = -inf for j > i     key j after query i is masked (top-left).
+  masks: S_ij = -inf outside a band key j is visible to query i when
+                                    diag_i - left <= j <= diag_i + right,
+                                    diag_i = i + Nk - Nq (query rows aligned
+                                    with the last Nq keys, as when new queries
+                                    attend over a cache of earlier keys). A
+                                    bound of None is absent. causal is
+                                    right = 0 (for Nq = Nk: key j > query i is
+                                    masked); a window of `left` earlier keys is
+                                    the local attention that the josueisai.com
+                                    page, section on what you gain and what
+                                    not, names as the way to cut the compute
+                                    of very long sequences.
   P = rowsoftmax(S)                 same page, section on the softmax trick:
                                     subtract the row maximum, divide by the sum
                                     of exponentials.
@@ -29,8 +40,9 @@ applied to the definition above, so the oracle is the exact gradient of its own
 forward):  dV = P^T dO;  dP = dO V^T;  D_i = sum_j P_ij dP_ij;
            dS = P * (dP - D 1^T);  dQ = scale dS K;  dK = scale dS^T Q.
 
-A fully masked row (never produced by the top-left causal mask with equal
-query and key lengths) is defined as O = 0, LSE = -inf, zero gradients.
+A fully masked row (with Nq > Nk under the causal mask, or a band that
+leaves a row no key) is defined as O = 0, LSE = -inf, zero gradients: the
+empty sum of exponentials is 0 and the row takes no part in any product.
 
 Rows may be processed in chunks to bound memory, but every query row always
 sees its whole key row at once: there is no online rescaling anywhere here.
@@ -49,13 +61,32 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q_rows: np.ndarray, row_idx: np.ndarray, k: np.ndarray,
-            scale: float, causal: bool) -> np.ndarray:
-    s = float(scale) * (q_rows @ k.T)
+def _band(causal: bool, window):
+    """(left, right) bounds of the visible band; None is unbounded."""
+    left, right = (None, None) if window is None else window
     if causal:
-        masked = np.arange(k.shape[0])[None, :] > row_idx[:, None]
-        s = np.where(masked, -np.inf, s)
-    return s
+        if right is not None and right != 0:
+            raise ValueError("causal sets right = 0; window gives another right bound")
+        right = 0
+    for w in (left, right):
+        if w is not None and w < 0:
+            raise ValueError("window bounds are >= 0 or None")
+    return left, right
+
+
+def _scores(q_rows: np.ndarray, row_idx: np.ndarray, k: np.ndarray,
+            scale: float, nq: int, left, right) -> np.ndarray:
+    s = float(scale) * (q_rows @ k.T)
+    if left is None and right is None:
+        return s
+    diag = row_idx + (k.shape[0] - nq)      # key aligned with each query row
+    j = np.arange(k.shape[0])[None, :]
+    masked = np.zeros(s.shape, dtype=bool)
+    if right is not None:
+        masked |= j > diag[:, None] + right
+    if left is not None:
+        masked |= j < diag[:, None] - left
+    return np.where(masked, -np.inf, s)
 
 
 def _softmax_rows(s: np.ndarray):
@@ -70,12 +101,14 @@ def _softmax_rows(s: np.ndarray):
     return p, m, l, dead
 
 
-def forward_head(q, k, v, scale: float, causal: bool = False, rows=None):
+def forward_head(q, k, v, scale: float, causal: bool = False, rows=None, window=None):
     """One head. q [Nq, d], k [Nk, d], v [Nk, dv] -> O [R, dv], LSE [R].
 
-    ``rows`` selects query rows (default: all); the causal mask uses the
-    absolute query index.
+    ``rows`` selects query rows (default: all); masks use the absolute query
+    index. ``window`` = (left, right) bounds the visible keys around each
+    row's aligned key (None = unbounded); ``causal`` sets right = 0.
     """
+    left, right = _band(causal, window)
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     if rows is None:
         rows = np.arange(q.shape[0])
@@ -84,7 +117,7 @@ def forward_head(q, k, v, scale: float, causal: bool = False, rows=None):
     lse = np.zeros(rows.size, dtype=np.float64)
     for c0 in range(0, rows.size, _ROW_CHUNK):
         idx = rows[c0:c0 + _ROW_CHUNK]
-        s = _scores(q[idx], idx, k, scale, causal)
+        s = _scores(q[idx], idx, k, scale, q.shape[0], left, right)
         p, m, l, dead = _softmax_rows(s)
         o[c0:c0 + idx.size] = p @ v
         with np.errstate(divide="ignore"):
@@ -92,8 +125,9 @@ def forward_head(q, k, v, scale: float, causal: bool = False, rows=None):
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool = False):
+def backward_head(q, k, v, do, scale: float, causal: bool = False, window=None):
     """One head: gradients of sum(O * dO) w.r.t. Q, K, V (LSE not differentiated)."""
+    left, right = _band(causal, window)
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     nq = q.shape[0]
     dq = np.zeros_like(q)
@@ -101,7 +135,7 @@ def backward_head(q, k, v, do, scale: float, causal: bool = False):
     dv = np.zeros_like(v)
     for c0 in range(0, nq, _ROW_CHUNK):
         idx = np.arange(c0, min(nq, c0 + _ROW_CHUNK))
-        s = _scores(q[idx], idx, k, scale, causal)
+        s = _scores(q[idx], idx, k, scale, nq, left, right)
         p, _, _, _ = _softmax_rows(s)
         g = do[idx]
         dv += p.T @ g
@@ -135,7 +169,7 @@ def _limit_blas(n_workers):
         return None
 
 
-def forward(q, k, v, scale: float, causal: bool = False, workers=None):
+def forward(q, k, v, scale: float, causal: bool = False, workers=None, window=None):
     """[..., N, d] batched forward; heads are independent and run in threads."""
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -144,7 +178,7 @@ def forward(q, k, v, scale: float, causal: bool = False, workers=None):
     lim = _limit_blas(n)
     try:
         with ThreadPoolExecutor(n) as ex:
-            res = list(ex.map(lambda i: forward_head(qh[i], kh[i], vh[i], scale, causal),
+            res = list(ex.map(lambda i: forward_head(qh[i], kh[i], vh[i], scale, causal, window=window),
                               range(qh.shape[0])))
     finally:
         if lim is not None:
@@ -154,7 +188,7 @@ def forward(q, k, v, scale: float, causal: bool = False, workers=None):
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool = False, workers=None):
+def backward(q, k, v, do, scale: float, causal: bool = False, workers=None, window=None):
     """[..., N, d] batched backward; returns dQ, dK, dV."""
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -164,7 +198,7 @@ def backward(q, k, v, do, scale: float, causal: bool = False, workers=None):
     lim = _limit_blas(n)
     try:
         with ThreadPoolExecutor(n) as ex:
-            res = list(ex.map(lambda i: backward_head(qh[i], kh[i], vh[i], gh[i], scale, causal),
+            res = list(ex.map(lambda i: backward_head(qh[i], kh[i], vh[i], gh[i], scale, causal, window=window),
                               range(qh.shape[0])))
     finally:
         if lim is not None:

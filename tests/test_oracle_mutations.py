@@ -18,7 +18,12 @@ import test_oracle_pins as pins
 MUTATIONS = [
     ("_scores", "float(scale) * (q_rows @ k.T)", "(q_rows @ k.T)"),
     ("_scores", "float(scale) * (q_rows @ k.T)", "float(scale) * (q_rows @ k.T) + 0.01"),
-    ("_scores", "[None, :] > row_idx", "[None, :] >= row_idx"),
+    ("_scores", "j > diag[:, None] + right", "j >= diag[:, None] + right"),
+    ("_scores", "j < diag[:, None] - left", "j <= diag[:, None] - left"),
+    ("_scores", "j < diag[:, None] - left", "j < diag[:, None] + left"),
+    ("_scores", "row_idx + (k.shape[0] - nq)", "row_idx"),
+    ("_scores", "row_idx + (k.shape[0] - nq)", "row_idx + (nq - k.shape[0])"),
+    ("_band", "        right = 0\n", "        right = None\n"),
     ("_softmax_rows", "m = s.max(axis=1)", "m = s.min(axis=1)"),
     ("_softmax_rows", "p = e / np.where(dead, 1.0, l)[:, None]", "p = e / np.where(dead, 1.0, l.max())"),
     ("forward_head", "m + np.log(l)", "np.log(l)"),
@@ -68,7 +73,7 @@ def test_each_planted_mistake_is_caught(monkeypatch, fn_name, old, new):
     mutant, ns = _mutated(fn_name, old, new)
     monkeypatch.setattr(oa, fn_name, mutant)
     # helpers called by other oracle functions are looked up in oa's globals
-    for name in ("_scores", "_softmax_rows"):
+    for name in ("_scores", "_softmax_rows", "_band"):
         if name == fn_name:
             ns[name] = mutant
     # the public entry points in oracle/__init__ are the same objects as oa's

@@ -27,7 +27,7 @@ _BIN = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul,
 
 
 def _eval(expr: str) -> float:
-    """Evaluate a closed form made of numbers, + - * /, unary -, log()."""
+    """Evaluate a closed form made of numbers, inf, + - * /, unary -, log()."""
     def ev(n):
         if isinstance(n, ast.Expression):
             return ev(n.body)
@@ -40,6 +40,8 @@ def _eval(expr: str) -> float:
         if (isinstance(n, ast.Call) and isinstance(n.func, ast.Name)
                 and n.func.id == "log" and len(n.args) == 1):
             return math.log(ev(n.args[0]))
+        if isinstance(n, ast.Name) and n.id == "inf":
+            return math.inf
         raise ValueError(f"unsupported expression: {expr!r}")
     return ev(ast.parse(expr, mode="eval"))
 
@@ -53,6 +55,11 @@ def _load_cases():
         return json.load(f)["cases"]
 
 
+def _window(case):
+    w = case.get("window")
+    return None if w is None else tuple(w)
+
+
 def _rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
@@ -62,7 +69,7 @@ def _rand(shape, seed):
 @pytest.mark.parametrize("case", _load_cases(), ids=lambda c: c["name"])
 def test_hand_worked_forward(case):
     q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
-    o, lse = oracle.forward_head(q, k, v, _eval(case["scale"]), case["causal"])
+    o, lse = oracle.forward_head(q, k, v, _eval(case["scale"]), case["causal"], window=_window(case))
     np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=1e-13)
 
@@ -70,7 +77,8 @@ def test_hand_worked_forward(case):
 @pytest.mark.parametrize("case", _load_cases(), ids=lambda c: c["name"])
 def test_hand_worked_backward(case):
     q, k, v, do = (_arr(case[n]) for n in ("q", "k", "v", "do"))
-    dq, dk, dv = oracle.backward_head(q, k, v, do, _eval(case["scale"]), case["causal"])
+    dq, dk, dv = oracle.backward_head(q, k, v, do, _eval(case["scale"]), case["causal"],
+                                      window=_window(case))
     np.testing.assert_allclose(dq, _arr(case["dq"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(dk, _arr(case["dk"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(dv, _arr(case["dv"]), rtol=0, atol=1e-13)
@@ -184,10 +192,152 @@ def test_large_scores_do_not_overflow():
 
 
 def test_fully_masked_row_reading():
-    # A query whose every key is masked (query index -1 under the causal rule)
-    q, k, v = _rand((1, 4), 30), _rand((3, 4), 31), _rand((3, 2), 32)
-    o, lse = oracle.forward_head(q, k, v, 1.0, causal=True, rows=np.array([-1]))
-    assert np.all(o == 0) and lse[0] == -np.inf
+    # Five queries over three keys under the causal mask: queries 0 and 1 are
+    # aligned before the first key and see nothing; a band that excludes a
+    # row's keys does the same.
+    q, k, v = _rand((5, 4), 30), _rand((3, 4), 31), _rand((3, 2), 32)
+    o, lse = oracle.forward_head(q, k, v, 1.0, causal=True)
+    assert np.all(o[:2] == 0) and np.all(lse[:2] == -np.inf)
+    assert np.all(np.isfinite(lse[2:]))
+    do = _rand((5, 2), 33)
+    dq, _, _ = oracle.backward_head(q, k, v, do, 1.0, causal=True)
+    assert np.all(dq[:2] == 0)
+
+
+# ------------------------------------- unequal lengths and banded masks ---
+
+def test_decode_rows_are_the_last_rows_of_square_causal():
+    # Nq queries over Nk keys with the causal mask are the last Nq rows of
+    # square causal attention whose last Nq queries are these (new tokens
+    # attending over a cache of earlier keys).
+    nk, nq, d = 40, 7, 8
+    q_full = _rand((nk, d), 60)
+    k, v = _rand((nk, d), 61), _rand((nk, 5), 62)
+    do = _rand((nq, 5), 63)
+    o_sq, lse_sq = oracle.forward_head(q_full, k, v, 0.3, causal=True)
+    o, lse = oracle.forward_head(q_full[-nq:], k, v, 0.3, causal=True)
+    np.testing.assert_allclose(o, o_sq[-nq:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_sq[-nq:], rtol=0, atol=1e-13)
+    # gradients: the square problem with dO zero on the first rows
+    do_full = np.zeros((nk, 5))
+    do_full[-nq:] = do
+    dq_sq, dk_sq, dv_sq = oracle.backward_head(q_full, k, v, do_full, 0.3, causal=True)
+    dq, dk, dv = oracle.backward_head(q_full[-nq:], k, v, do, 0.3, causal=True)
+    np.testing.assert_allclose(dq, dq_sq[-nq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_sq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_sq, rtol=0, atol=1e-12)
+
+
+def test_more_queries_than_keys_pads_dead_rows_in_front():
+    nq, nk, d = 11, 6, 4
+    q, k, v = _rand((nq, d), 64), _rand((nk, d), 65), _rand((nk, 3), 66)
+    o, lse = oracle.forward_head(q, k, v, 0.7, causal=True)
+    o_sq, lse_sq = oracle.forward_head(q[nq - nk:], k, v, 0.7, causal=True)
+    assert np.all(o[:nq - nk] == 0) and np.all(lse[:nq - nk] == -np.inf)
+    np.testing.assert_allclose(o[nq - nk:], o_sq, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[nq - nk:], lse_sq, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("nq,nk", [(5, 9), (9, 5), (8, 8)])
+def test_unmasked_unequal_lengths_match_torch_sdpa(nq, nk):
+    torch = pytest.importorskip("torch")
+    q, k, v = _rand((nq, 6), 67), _rand((nk, 6), 68), _rand((nk, 3), 69)
+    o, lse = oracle.forward_head(q, k, v, 0.4)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    o_ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], scale=0.4)[0]
+    np.testing.assert_allclose(o, o_ref.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(0.4 * tq @ tk.T, dim=1).numpy(), rtol=0, atol=1e-13)
+
+
+def test_window_of_zero_returns_the_aligned_value_row():
+    # left = right = 0: each query sees exactly its aligned key, so O_i is
+    # that key's value row and LSE_i its scaled score
+    nq, nk, d = 6, 10, 5
+    q, k, v = _rand((nq, d), 70), _rand((nk, d), 71), _rand((nk, 4), 72)
+    o, lse = oracle.forward_head(q, k, v, 0.5, window=(0, 0))
+    j = np.arange(nq) + nk - nq
+    np.testing.assert_allclose(o, v[j], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * np.einsum("id,id->i", q, k[j]), rtol=0, atol=1e-14)
+
+
+def test_window_wider_than_the_keys_is_the_plain_mask():
+    nq, nk, d = 7, 12, 4
+    q, k, v = _rand((nq, d), 73), _rand((nk, d), 74), _rand((nk, 3), 75)
+    for causal in (False, True):
+        o_ref, lse_ref = oracle.forward_head(q, k, v, 0.6, causal=causal)
+        o, lse = oracle.forward_head(q, k, v, 0.6, window=(nk + nq, 0 if causal else nk + nq))
+        np.testing.assert_array_equal(o, o_ref)
+        np.testing.assert_array_equal(lse, lse_ref)
+
+
+@pytest.mark.parametrize("window", [(3, 0), (0, 2), (2, 5), (None, 1), (4, None)])
+@pytest.mark.parametrize("nq,nk", [(9, 9), (5, 12), (12, 5)])
+def test_banded_rows_equal_torch_sdpa_over_their_key_range(window, nq, nk):
+    # Each row of banded attention is plain attention (PyTorch's float64 CPU
+    # SDPA) of that query over the contiguous range of keys the band keeps.
+    torch = pytest.importorskip("torch")
+    q, k, v = _rand((nq, 4), 76), _rand((nk, 4), 77), _rand((nk, 3), 78)
+    o, lse = oracle.forward_head(q, k, v, 0.8, window=window)
+    left, right = window
+    for i in range(nq):
+        a = i + nk - nq
+        lo = 0 if left is None else max(0, a - left)
+        hi = nk - 1 if right is None else min(nk - 1, a + right)
+        if hi < lo:
+            assert np.all(o[i] == 0) and lse[i] == -np.inf
+            continue
+        tq = torch.from_numpy(q[i:i + 1])
+        tk, tv = torch.from_numpy(k[lo:hi + 1]), torch.from_numpy(v[lo:hi + 1])
+        o_ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], scale=0.8)[0]
+        np.testing.assert_allclose(o[i], o_ref[0].numpy(), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[i], torch.logsumexp(0.8 * tq @ tk.T, dim=1).item(), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window,nq,nk", [((2, 0), 6, 6), ((1, 1), 4, 7), ((None, 0), 7, 4)])
+def test_banded_backward_matches_central_finite_differences(window, nq, nk):
+    d, dv_ = 3, 2
+    q, k, v = _rand((nq, d), 79), _rand((nk, d), 80), _rand((nk, dv_), 81)
+    do = _rand((nq, dv_), 82)
+    scale = 0.9
+    dq, dk, dv = oracle.backward_head(q, k, v, do, scale, window=window)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward_head(q_, k_, v_, scale, window=window)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if a is x else a for a in (q, k, v)]
+            args_m = [xm if a is x else a for a in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("window,nq,nk", [((3, 0), 16, 16), ((None, 0), 20, 9), ((2, 4), 9, 20)])
+def test_banded_gradient_invariants(window, nq, nk):
+    # rows of dS sum to 0, hence sum_j dK_j = 0; sum_j dV_j = sum of dO over
+    # the rows that see at least one key
+    q, k, v = _rand((nq, 5), 83), _rand((nk, 5), 84), _rand((nk, 3), 85)
+    do = _rand((nq, 3), 86)
+    _, lse = oracle.forward_head(q, k, v, 0.5, window=window)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, 0.5, window=window)
+    live = np.isfinite(lse)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do[live].sum(axis=0), atol=1e-12)
+    assert np.all(dq[~live] == 0)
+
+
+def test_band_arguments_are_checked():
+    q = _rand((3, 2), 87)
+    with pytest.raises(ValueError):
+        oracle.forward_head(q, q, q, 1.0, causal=True, window=(2, 1))
+    with pytest.raises(ValueError):
+        oracle.forward_head(q, q, q, 1.0, window=(-1, 0))
 
 
 # -------------------------------------------- blockwise replay (the pages) ---
