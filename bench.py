@@ -9,6 +9,11 @@ self-attention shape B=1, H=32, N=8192, d=128, bf16, non-causal; its inputs
 
 FLOPs follow the attention convention: forward 4*N^2*d per head (halved under
 causal masking), backward 2.5x that. Prints ONE JSON line.
+
+`--suite` instead times the general-shape workloads (a sliding window, new
+queries over a long key cache, fp16, a [B, N, H, d] layout) through
+fa_fwd_ex / fa_bwd_ex and prints one JSON line per workload; there FLOPs are
+4*d per visible (query, key) pair, counted exactly for the mask.
 """
 from __future__ import annotations
 
@@ -33,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # counter passes summarised in this file (scaled by a copy of known size). The
 # figure is only reported while the kernel's sources hash to the recorded value.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_n8192_d128_hbm_bytes.md")
-FWD_SOURCES = ("fa_device.h", "fa_fwd_bf16.hip", "fa_kernels.h")
+FWD_SOURCES = ("fa_device.h", "fa_fwd_mfma.hip", "fa_kernels.h")
 
 
 def fwd_source_sha256():
@@ -73,10 +78,84 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads the CPU oracle times (at most B*H)")
     ap.add_argument("--fwd-only", action="store_true", help="time fa_fwd alone (profiling aid)")
+    ap.add_argument("--suite", action="store_true",
+                    help="time the general-shape workloads instead (one JSON line each)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (read + write) instead, to scale "
                          "hardware byte counters")
     return ap.parse_args()
+
+
+def visible_pairs(nq, nk, window):
+    """(query, key) pairs a band mask keeps: query i sees keys
+    [i + nk - nq - left, i + nk - nq + right] within [0, nk)."""
+    import numpy as np
+    left, right = window
+    a = np.arange(nq, dtype=np.int64) + (nk - nq)
+    lo = np.zeros(nq, np.int64) if left is None else np.maximum(0, a - left)
+    hi = np.full(nq, nk - 1, np.int64) if right is None else np.minimum(nk - 1, a + right)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+SUITE = ("window_n16384_d128_w1024", "prefill_q512_k16384_d128", "fp16_n8192_d128", "bnhd_n8192_d128")
+
+
+def run_suite(args):
+    """Event-timed fa_fwd_ex / fa_bwd_ex on each general-shape workload."""
+    import torch
+    from exact_attention_122_amd import fa, inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name in SUITE:
+        w = inputs.WORKLOADS[name]
+        B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+        nk = w.get("nk", N)
+        window = w.get("window", (None, 0) if w["causal"] else (None, None))
+        scale = inputs.default_scale(d)
+        g = inputs.generate_workload(name)
+        q, k, v, do = (g[x].to_torch(dev) for x in ("q", "k", "v", "do"))
+        layout = w.get("layout", "bhnd")
+        if layout == "bnhd":  # [B, N, H, d] memory seen as [B, H, N, d]
+            q, k, v, do = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v, do))
+            o = torch.empty(B, N, H, d, dtype=q.dtype, device=dev).transpose(1, 2)
+            grads = [torch.empty(B, n, H, d, dtype=q.dtype, device=dev).transpose(1, 2) for n in (N, nk, nk)]
+        else:
+            o = torch.empty_like(q)
+            grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, fa.fa_bwd_ex_workspace_bytes(B, H, N, nk, d, fa._dtype_code(q))),
+                         dtype=torch.uint8, device=dev)
+        wl = -1 if window[0] is None else window[0]
+        wr = -1 if window[1] is None else window[1]
+
+        def fwd():
+            fa.fa_fwd_ex(q, k, v, window=(wl, wr), scale=scale, out=o, lse=lse)
+
+        def bwd():
+            fa.fa_bwd_ex(q, k, v, o, do, lse, window=(wl, wr), scale=scale, dq=grads[0], dk=grads[1],
+                         dv=grads[2], workspace=ws)
+
+        res = {}
+        pairs = visible_pairs(N, nk, window) * B * H
+        for tag, fn, flops in (("fwd", fwd, 4.0 * d * pairs), ("bwd", bwd, 10.0 * d * pairs)):
+            for _ in range(args.warmup):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for i in range(args.steps):
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+            med = ms[len(ms) // 2]
+            res[tag] = {"ms": round(med, 4), "tflops": round(flops / med / 1e9, 2),
+                        "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        print(json.dumps({"suite": name, "dtype": w["dtype"], "layout": layout,
+                          "config": {"B": B, "H": H, "Nq": N, "Nk": nk, "d": d,
+                                     "window": [wl, wr], "seed": w["seed"]},
+                          "visible_pairs": pairs, "flops_fwd": 4.0 * d * pairs, **res,
+                          "peak": PEAK_BF16_TFLOPS}), flush=True)
 
 
 def calibrate_copy(mib):
@@ -119,6 +198,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path: heads are independent and would shard with no exchange.", file=sys.stderr)
         sys.exit(2)
+    if args.suite:
+        run_suite(args)
+        return
 
     import torch
     from exact_attention_122_amd import fa, inputs
@@ -185,7 +267,7 @@ def main():
 
     # roofline of fa_fwd's kernel: algorithmic FLOPs per launch / event-timed launch duration
     ach = f_fwd / fwd_avg / 1e9
-    kname = f"fwd_bf16_kernel<{d},{'causal' if causal else 'full'}>"
+    kname = f"fwd_kernel<bf16,{d},{'upper' if causal else 'none'}>"
     roof = {"kernel": f"{kname} (fa_fwd)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),

@@ -1,0 +1,589 @@
+// Backward attention, bf16 or fp16 in and out, fp32 accumulation, MFMA on gfx950.
+//
+// The backward keeps no score or probability matrix: both are recomputed from
+// Q, K and the saved log-sum-exp ('FlashAttention', josueisai.com, section on
+// recomputing instead of remembering), P = exp(scale * Q K^T - LSE). The
+// gradient formulas are the chain rule of the forward definition:
+//   dV = P^T dO;  dP = dO V^T;  D_i = sum_k dO_ik O_ik = sum_j P_ij dP_ij;
+//   dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
+//
+// Three launches on one stream, no atomics, deterministic:
+//  1. row_stats_kernel: per query row, D_i from O and dO, and LSE_i * log2(e)
+//     (so the kernels below form P with one FMA and exp2). Stored per head in
+//     64-row tiles [64 x LSE*log2e | 64 x D] (512 bytes, zeros past N).
+//  2. dkdv_kernel: a work-group owns 128 keys (32 per wave, K and V rows held
+//     in registers) and streams 64-row query tiles (Q, dO and their row
+//     statistics) through LDS. Scores are computed as S = Q K^T so each lane
+//     holds one key; P and dS then feed dV += P^T dO and dK += dS^T Q directly
+//     as A operands, with dO and Q read transposed out of LDS
+//     (ds_read_b64_tr_b16).
+//  3. dq_kernel: a work-group owns 128 query rows (32 per wave, Q and dO rows
+//     in registers) and streams 64-key K/V tiles through LDS. Scores are
+//     computed transposed, S^T = K Q^T, so each lane holds one query (its LSE
+//     and D are per-lane scalars); dS^T feeds dQ^T += K^T dS^T as the B
+//     operand, with K read transposed out of LDS.
+// Tiles are copied global -> LDS directly (no staging registers). Query rows
+// past the end arrive as zeros with zero statistics, so a zero Q / dO row
+// contributes exactly nothing to dK and dV; keys past the end are masked on
+// the last tile of dq_kernel. Shapes, strides and band masks follow the
+// forward pass: query i is aligned with key i + nk - nq, a band keeps keys
+// [i + nk - nq - wl, i + nk - nq + wr], each work-group visits only the tiles
+// its band touches, and tiles across a band edge set P = 0 on dead pairs. A
+// query row that saw no key (LSE = -inf) gets P = 0 on every key.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;            // rows per LDS tile
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerBlock = 128;   // keys (dkdv) or queries (dq) per work-group
+constexpr int kStatTileBytes = 2 * kTile * 4;
+
+struct BwdParams {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* dout;
+  const float* stats;  // per head: nq_pad / 64 tiles of [64 LSE*log2e | 64 D]
+  bf16_t* dq;
+  bf16_t* dk;
+  bf16_t* dv;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, do_sb, do_sh;  // batch / head strides (elements)
+  long long dq_sb, dq_sh, dk_sb, dk_sh, dv_sb, dv_sh;
+  int q_sr, k_sr, v_sr, do_sr, dq_sr, dk_sr, dv_sr;          // row strides (elements)
+  int heads;
+  int nq, nk;
+  int nq_pad;    // nq rounded up to a multiple of 64
+  int diag;      // nk - nq: the key aligned with query 0
+  int wl, wr;    // band (banded kernels only), both >= 0
+  int nkb, nqb;  // key blocks (dkdv) and query blocks (dq) per head
+  float c;       // scale * log2(e)
+  float scale;
+};
+
+// Per-head base of a strided tensor.
+__device__ __forceinline__ const bf16_t* head_base(const bf16_t* t, long long sb, long long sh, int heads, int head) {
+  const int b = head / heads;
+  return t + b * sb + (head - b * heads) * sh;
+}
+
+// One thread group of D/8 lanes per padded query row: D_i = dO_i . O_i and
+// LSE_i * log2(e). A row that saw no key (LSE = -inf) stores +inf, so the
+// kernels' exp2(c s - L) is 0 for it on every key.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(const bf16_t* o, const bf16_t* dout, const float* lse,
+                                                             float* stats, Strides so, Strides sdo, int heads, int nq,
+                                                             int nq_pad, long long padded_rows) {
+  constexpr int kLanesPerRow = D / 8;
+  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long prow = gid / kLanesPerRow;
+  const int part = (int)(gid % kLanesPerRow);
+  const int head = (int)(prow / nq_pad);
+  const int r = (int)(prow - (long long)head * nq_pad);
+  const bool valid = prow < padded_rows && r < nq;
+  float acc = 0.f;
+  if (valid) {
+    const int b = head / heads, h = head - b * heads;
+    const u32x4 x = *(const u32x4*)(o + b * so.b + h * so.h + r * so.r + part * 8);
+    const u32x4 y = *(const u32x4*)(dout + b * sdo.b + h * sdo.h + r * sdo.r + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(E::lo(x[i]), E::lo(y[i]), acc);
+      acc = fmaf(E::hi(x[i]), E::hi(y[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (prow < padded_rows && part == 0) {
+    float* tile = stats + ((long long)head * nq_pad + (r & ~(kTile - 1))) * 2;
+    float l2 = 0.f;
+    if (valid) {
+      const float x = lse[(long long)head * nq + r];
+      l2 = x == -INFINITY ? INFINITY : x * kLog2e;
+    }
+    tile[r & (kTile - 1)] = l2;
+    tile[kTile + (r & (kTile - 1))] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV ---
+
+// One 64-query tile against the wave's 32 keys. With a band, `masked` tiles
+// (across a band edge) set P = 0 where query row qr is outside this lane's
+// [q_lo, q_hi]. Without one the tile holds no masking code at all: query rows
+// past the end are zero rows with zero statistics and add nothing.
+template <typename E, int D, int MASK>
+__device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, const float* st,
+                                          const RowRead<D>& rrd, const TrRead<D>& trd, const bf16x8 (&kf)[D / 16],
+                                          const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                          float c, int q0, int q_lo, int q_hi, int lane, bool masked) {
+  const int hw = lane >> 5;
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    s[qb] = f32x16{};
+    dp[qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s[qb] = E::mfma(rrd(qt, qb, ks), kf[ks], s[qb]);
+      dp[qb] = E::mfma(rrd(dt, qb, ks), vf[ks], dp[qb]);
+    }
+  }
+  // lane holds one key; register r of block qb holds query
+  // q0 + 32 qb + 8 (r / 4) + 4 hw + r % 4
+  bf16x8 pa[4], da[4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = qb * 32 + 8 * g + 4 * hw;
+      const f32x4 Lv = *(const FA_LDS f32x4*)((const FA_LDS float*)st + r0);
+      const f32x4 Rv = *(const FA_LDS f32x4*)((const FA_LDS float*)st + kTile + r0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 4 * g + rr;
+        float arg = fmaf(s[qb][i], c, -Lv[rr]);
+        if (MASK != kMaskNone && masked) {
+          const int qr = q0 + r0 + rr;
+          arg = (qr < q_lo || (MASK == kMaskBand && qr > q_hi)) ? -INFINITY : arg;
+        }
+        const float pv = fast_exp2(arg);
+        const int t = qb * 2 + (g >> 1), e = 4 * (g & 1) + rr;
+        pa[t][e] = E::cvt(pv);
+        da[t][e] = E::cvt(pv * (dp[qb][i] - Rv[rr]));
+      }
+    }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dv[db] = E::mfma(pa[t], trd(dt, t, db), dv[db]);
+      dk[db] = E::mfma(da[t], trd(qt, t, db), dk[db]);
+    }
+}
+
+struct QTileBufs {
+  bf16_t* q;
+  bf16_t* d;
+  float* st;
+};
+
+template <int D>
+struct DkdvCopy {
+  TileDma<kTile, D, kThreads> dma;
+  __amdgpu_buffer_rsrc_t qrs, drs, srs;
+  uint32_t q_stride, d_stride;  // bytes between rows of Q and dO
+  int wave, lane;
+  // query tile starting at row q0 -> LDS
+  __device__ __forceinline__ void issue(const QTileBufs& b, int q0) const {
+    dma.issue(qrs, b.q, q0, q_stride);
+    dma.issue(drs, b.d, q0, d_stride);
+    if (wave == 0 && lane < kStatTileBytes / 16) {
+      FA_LDS void* dst = (FA_LDS void*)(FA_LDS float*)b.st;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, dst, 16, (uint32_t)(q0 / kTile) * kStatTileBytes + 16 * lane,
+                                               0, 0, 0);
+    }
+  }
+};
+
+// One query tile for this wave's keys wk0 .. wk0 + 31. With a band, rows with
+// q + diag in [wk0 - wr, wk0 + 31 + wl] see some of the keys and rows with
+// q + diag in [wk0 + 31 - wr, wk0 + wl] see all of them.
+template <typename E, int D, int MASK>
+__device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur, const QTileBufs& nxt,
+                                            const DkdvCopy<D>& cp, const RowRead<D>& rrd, const TrRead<D>& trd,
+                                            const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
+                                            f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const BwdParams& p,
+                                            int wk0, int q_lo, int q_hi, int lane) {
+  const int q0 = t * kTile;
+  if (t + 1 < t_end) cp.issue(nxt, q0 + kTile);
+  bool live = wk0 < p.nk, masked = false;
+  if (MASK != kMaskNone) {
+    live = live && q0 + kTile - 1 + p.diag >= wk0 - p.wr;
+    masked = q0 + p.diag < wk0 + 31 - p.wr;
+    if (MASK == kMaskBand) {
+      live = live && q0 + p.diag <= wk0 + 31 + p.wl;
+      masked = masked || q0 + kTile - 1 + p.diag > wk0 + p.wl;
+    }
+  }
+  if (live) dkdv_tile<E, D, MASK>(cur.q, cur.d, cur.st, rrd, trd, kf, vf, dk, dv, p.c, q0, q_lo, q_hi, lane, masked);
+  wait_vmem();
+  __syncthreads();
+}
+
+template <typename E, int D, int MASK>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds1[kTile * D];
+  __shared__ __attribute__((aligned(16))) float s_lds0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) float s_lds1[2 * kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = lane >> 5;
+  const int col = lane & 31;
+  const int nq = p.nq, nk = p.nk;
+
+  const int logical = xcd_logical_block(blockIdx.x, (int)gridDim.x);
+  const int head = logical / p.nkb;
+  const int kblk = logical - head * p.nkb;
+  const int key_wg = kblk * kRowsPerBlock;
+  const int wk0 = key_wg + wave * kRowsPerWave;
+  const int key = wk0 + col;
+  // query rows that see this lane's key: [key - diag - wr, key - diag + wl]
+  const int q_lo = key - p.diag - p.wr, q_hi = key - p.diag + p.wl;
+
+  // query tiles of this work-group's band
+  int t_begin = 0, t_end = (nq + kTile - 1) / kTile;
+  if (MASK != kMaskNone) {
+    const int r_lo = max(0, key_wg - p.diag - p.wr);
+    const int r_hi = min(nq - 1, key_wg + kRowsPerBlock - 1 - p.diag + p.wl);
+    t_begin = r_lo / kTile;
+    t_end = r_hi < r_lo ? t_begin : r_hi / kTile + 1;
+  }
+
+  const bf16_t* qh = head_base(p.q, p.q_sb, p.q_sh, p.heads, head);
+  const bf16_t* dh = head_base(p.dout, p.do_sb, p.do_sh, p.heads, head);
+  const bf16_t* kh = head_base(p.k, p.k_sb, p.k_sh, p.heads, head);
+  const bf16_t* vh = head_base(p.v, p.v_sb, p.v_sh, p.heads, head);
+  DkdvCopy<D> cp;
+  cp.dma.init(wave, lane);
+  cp.qrs = rows_rsrc<D>(qh, nq, 2u * p.q_sr);
+  cp.drs = rows_rsrc<D>(dh, nq, 2u * p.do_sr);
+  cp.srs = make_rsrc(p.stats + (long long)head * p.nq_pad * 2, (uint32_t)p.nq_pad * 8);
+  cp.q_stride = 2u * p.q_sr;
+  cp.d_stride = 2u * p.do_sr;
+  cp.wave = wave;
+  cp.lane = lane;
+  const QTileBufs b0{q_lds0, d_lds0, s_lds0}, b1{q_lds1, d_lds1, s_lds1};
+  if (t_begin < t_end) cp.issue(b0, t_begin * kTile);
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 kx = u32x4{0u, 0u, 0u, 0u}, vx = kx;
+    if (key < nk) {
+      kx = *(const u32x4*)(kh + (long long)key * p.k_sr + 16 * ks + 8 * hw);
+      vx = *(const u32x4*)(vh + (long long)key * p.v_sr + 16 * ks + 8 * hw);
+    }
+    kf[ks] = __builtin_bit_cast(bf16x8, kx);
+    vf[ks] = __builtin_bit_cast(bf16x8, vx);
+  }
+  RowRead<D> rrd;
+  rrd.init(lane);
+  TrRead<D> trd;
+  trd.init(lane);
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  wait_vmem();
+  __syncthreads();
+  for (int t = t_begin; t < t_end; t += 2) {
+    dkdv_step<E, D, MASK>(t, t_end, b0, b1, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane);
+    if (t + 1 < t_end)
+      dkdv_step<E, D, MASK>(t + 1, t_end, b1, b0, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane);
+  }
+
+  // lane holds d = 32 db + col for keys wk0 + 8 g + 4 hw + rr
+  bf16_t* dkh = (bf16_t*)head_base(p.dk, p.dk_sb, p.dk_sh, p.heads, head);
+  bf16_t* dvh = (bf16_t*)head_base(p.dv, p.dv_sb, p.dv_sh, p.heads, head);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int kr = wk0 + 8 * g + 4 * hw + rr;
+        if (kr < nk) {
+          dkh[(long long)kr * p.dk_sr + 32 * db + col] = __builtin_bit_cast(bf16_t, E::cvt(dk[db][4 * g + rr] * p.scale));
+          dvh[(long long)kr * p.dv_sr + 32 * db + col] = __builtin_bit_cast(bf16_t, E::cvt(dv[db][4 * g + rr]));
+        }
+      }
+}
+
+// -------------------------------------------------------------------- dQ ---
+
+// One 64-key tile against the wave's 32 query rows. `masked` tiles set P = 0
+// for keys past the end and, with a band, outside this lane's [k_lo, k_hi].
+// MASK_CODE says whether the tile carries that code at all: the unmasked main
+// loop of a kernel without band has no branch in the middle of its tiles.
+template <typename E, int D, int MASK, bool MASK_CODE>
+__device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, const RowRead<D>& rrd,
+                                        const TrRead<D>& trd, const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32], float lse2, float drow,
+                                        float c, int key0, int k_lo, int k_hi, int lane, bool masked) {
+  const int hw = lane >> 5;
+  f32x16 s[2], dpt[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+    dpt[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s[kb] = E::mfma(rrd(kt, kb, ks), qf[ks], s[kb]);
+      dpt[kb] = E::mfma(rrd(vt, kb, ks), df[ks], dpt[kb]);
+    }
+  }
+  bf16x8 ds[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arg = fmaf(s[kb][i], c, -lse2);
+      if (MASK_CODE && masked) {
+        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hw + (i & 3);
+        arg = (key > k_hi || (MASK == kMaskBand && key < k_lo)) ? -INFINITY : arg;
+      }
+      const float pv = fast_exp2(arg);
+      ds[kb * 2 + (i >> 3)][i & 7] = E::cvt(pv * (dpt[kb][i] - drow));
+    }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dq[db] = E::mfma(trd(kt, t, db), ds[t], dq[db]);
+}
+
+template <typename E, int D, int MASK, bool MASK_CODE>
+__device__ __forceinline__ void dq_step(int j, int n_tiles, int key_base, const bf16_t* kt, const bf16_t* vt,
+                                        bf16_t* kn, bf16_t* vn, const TileDma<kTile, D, kThreads>& dma,
+                                        __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                        const RowRead<D>& rrd, const TrRead<D>& trd, const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32], float lse2, float drow,
+                                        const BwdParams& p, int k_lo, int k_hi, int wq0, int lane) {
+  const int key0 = key_base + j * kTile;
+  if (j + 1 < n_tiles) {
+    dma.issue(krs, kn, key0 + kTile, 2u * p.k_sr);
+    dma.issue(vrs, vn, key0 + kTile, 2u * p.v_sr);
+  }
+  // the wave's rows are wq0 .. wq0 + 31 (rows past nq are never stored)
+  bool live = wq0 < p.nq, masked = key0 + kTile > p.nk;
+  if (MASK != kMaskNone) {
+    live = live && key0 <= wq0 + 31 + p.diag + p.wr;
+    masked = masked || key0 + kTile - 1 > wq0 + p.diag + p.wr;
+    if (MASK == kMaskBand) {
+      live = live && key0 + kTile - 1 >= wq0 + p.diag - p.wl;
+      masked = masked || key0 < wq0 + 31 + p.diag - p.wl;
+    }
+  }
+  if (live) dq_tile<E, D, MASK, MASK_CODE>(kt, vt, rrd, trd, qf, df, dq, lse2, drow, p.c, key0, k_lo, k_hi, lane, masked);
+  wait_vmem();
+  __syncthreads();
+}
+
+template <typename E, int D, int MASK>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
+  constexpr bool BAND = MASK != kMaskNone;
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kTile * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = lane >> 5;
+  const int col = lane & 31;
+  const int nq = p.nq, nk = p.nk;
+
+  const int logical = xcd_logical_block(blockIdx.x, (int)gridDim.x);
+  const int head = logical / p.nqb;
+  int qblk = logical - head * p.nqb;
+  if (BAND) qblk = p.nqb - 1 - qblk;  // longest rows first under a causal band
+  const int q_row0 = qblk * kRowsPerBlock;
+  const int wq0 = q_row0 + wave * kRowsPerWave;
+  const int qi = wq0 + col;
+  // live keys of this lane's row: [k_lo, k_hi]
+  const int k_lo = BAND ? qi + p.diag - p.wl : 0;
+  const int k_hi = BAND ? min(nk - 1, qi + p.diag + p.wr) : nk - 1;
+
+  // key tiles of this work-group's band
+  const int q_last = min(nq, q_row0 + kRowsPerBlock) - 1;
+  int key_base = 0, n_tiles = (nk + kTile - 1) / kTile;
+  if (BAND) {
+    const int c_lo = max(0, q_row0 + p.diag - p.wl);
+    const int c_hi = min(nk - 1, q_last + p.diag + p.wr);
+    key_base = c_lo / kTile * kTile;
+    n_tiles = c_hi < c_lo ? 0 : (c_hi - key_base) / kTile + 1;
+  }
+
+  const bf16_t* qh = head_base(p.q, p.q_sb, p.q_sh, p.heads, head);
+  const bf16_t* dh = head_base(p.dout, p.do_sb, p.do_sh, p.heads, head);
+  const bf16_t* kh = head_base(p.k, p.k_sb, p.k_sh, p.heads, head);
+  const bf16_t* vh = head_base(p.v, p.v_sb, p.v_sh, p.heads, head);
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc<D>(kh, nk, 2u * p.k_sr);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc<D>(vh, nk, 2u * p.v_sr);
+  TileDma<kTile, D, kThreads> dma;
+  dma.init(wave, lane);
+  if (n_tiles > 0) {
+    dma.issue(krs, k_lds0, key_base, 2u * p.k_sr);
+    dma.issue(vrs, v_lds0, key_base, 2u * p.v_sr);
+  }
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 qx = u32x4{0u, 0u, 0u, 0u}, dx = qx;
+    if (qi < nq) {
+      qx = *(const u32x4*)(qh + (long long)qi * p.q_sr + 16 * ks + 8 * hw);
+      dx = *(const u32x4*)(dh + (long long)qi * p.do_sr + 16 * ks + 8 * hw);
+    }
+    qf[ks] = __builtin_bit_cast(bf16x8, qx);
+    df[ks] = __builtin_bit_cast(bf16x8, dx);
+  }
+  float lse2 = 0.f, drow = 0.f;
+  if (qi < nq) {
+    const float* st = p.stats + ((long long)head * p.nq_pad + (qi & ~(kTile - 1))) * 2;
+    lse2 = st[qi & (kTile - 1)];
+    drow = st[kTile + (qi & (kTile - 1))];
+  }
+  RowRead<D> rrd;
+  rrd.init(lane);
+  TrRead<D> trd;
+  trd.init(lane);
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  wait_vmem();
+  __syncthreads();
+  // Without a band only a ragged last tile needs masking (a zero K row past
+  // the end would get p = exp2(-LSE log2 e), which overflows for very
+  // negative LSE): it runs after the main loop, in a copy of the step that
+  // has the masking code.
+  const int n_main = BAND ? n_tiles : min(n_tiles, nk / kTile);
+  for (int j = 0; j < n_main; j += 2) {
+    dq_step<E, D, MASK, BAND>(j, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf, df,
+                              dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+    if (j + 1 < n_main)
+      dq_step<E, D, MASK, BAND>(j + 1, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+  }
+  if (!BAND && n_main < n_tiles) {
+    if (n_main & 1)
+      dq_step<E, D, MASK, true>(n_main, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+    else
+      dq_step<E, D, MASK, true>(n_main, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+  }
+
+  if (qi < nq) {
+    bf16_t* row = (bf16_t*)head_base(p.dq, p.dq_sb, p.dq_sh, p.heads, head) + (long long)qi * p.dq_sr;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack2<E>(dq[db][4 * g] * p.scale, dq[db][4 * g + 1] * p.scale);
+        w.y = pack2<E>(dq[db][4 * g + 2] * p.scale, dq[db][4 * g + 3] * p.scale);
+        *(uint2*)(row + db * 32 + 8 * g + 4 * hw) = w;
+      }
+  }
+}
+
+#define FA_BWD_INSTANCES(E, D)                                                                             \
+  template __global__ void dkdv_kernel<E, D, kMaskNone>(BwdParams);                                       \
+  template __global__ void dkdv_kernel<E, D, kMaskUpper>(BwdParams);                                      \
+  template __global__ void dkdv_kernel<E, D, kMaskBand>(BwdParams);                                       \
+  template __global__ void dq_kernel<E, D, kMaskNone>(BwdParams);                                         \
+  template __global__ void dq_kernel<E, D, kMaskUpper>(BwdParams);                                        \
+  template __global__ void dq_kernel<E, D, kMaskBand>(BwdParams);                                         \
+  template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
+                                                  Strides, int, int, int, long long);
+FA_BWD_INSTANCES(Bf16, 64)
+FA_BWD_INSTANCES(Bf16, 128)
+FA_BWD_INSTANCES(F16, 64)
+FA_BWD_INSTANCES(F16, 128)
+#undef FA_BWD_INSTANCES
+
+template <typename E, int D, int MASK>
+hipError_t launch(const BwdArgs& a) {
+  const Geometry& g = a.g;
+  BwdParams p;
+  p.q = (const bf16_t*)a.q;
+  p.k = (const bf16_t*)a.k;
+  p.v = (const bf16_t*)a.v;
+  p.dout = (const bf16_t*)a.dout;
+  p.stats = a.workspace;
+  p.dq = (bf16_t*)a.dq;
+  p.dk = (bf16_t*)a.dk;
+  p.dv = (bf16_t*)a.dv;
+  p.q_sb = a.sq.b, p.q_sh = a.sq.h, p.q_sr = (int)a.sq.r;
+  p.k_sb = a.sk.b, p.k_sh = a.sk.h, p.k_sr = (int)a.sk.r;
+  p.v_sb = a.sv.b, p.v_sh = a.sv.h, p.v_sr = (int)a.sv.r;
+  p.do_sb = a.sdo.b, p.do_sh = a.sdo.h, p.do_sr = (int)a.sdo.r;
+  p.dq_sb = a.sdq.b, p.dq_sh = a.sdq.h, p.dq_sr = (int)a.sdq.r;
+  p.dk_sb = a.sdk.b, p.dk_sh = a.sdk.h, p.dk_sr = (int)a.sdk.r;
+  p.dv_sb = a.sdv.b, p.dv_sh = a.sdv.h, p.dv_sr = (int)a.sdv.r;
+  p.heads = g.heads;
+  p.nq = g.nq;
+  p.nk = g.nk;
+  p.nq_pad = (g.nq + kTile - 1) / kTile * kTile;
+  p.diag = g.nk - g.nq;
+  // an absent bound becomes one no key can reach
+  p.wl = g.wl < 0 ? g.nq + g.nk : g.wl;
+  p.wr = g.wr < 0 ? g.nq + g.nk : g.wr;
+  p.nkb = (g.nk + kRowsPerBlock - 1) / kRowsPerBlock;
+  p.nqb = (g.nq + kRowsPerBlock - 1) / kRowsPerBlock;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+  const long long bh = (long long)g.batch * g.heads;
+
+  // with no query row, dK = dV = 0 and the statistics and dQ launches have
+  // no work; with no key, dQ = 0 and dkdv has none
+  const long long padded_rows = bh * p.nq_pad;
+  if (padded_rows > 0) {
+    const long long stat_blocks = (padded_rows * (D / 8) + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((row_stats_kernel<E, D>), dim3((unsigned)stat_blocks), dim3(kThreads), 0, a.stream,
+                       (const bf16_t*)a.o, p.dout, a.lse, a.workspace, a.so, a.sdo, g.heads, g.nq, p.nq_pad,
+                       padded_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nkb > 0) {
+    hipLaunchKernelGGL((dkdv_kernel<E, D, MASK>), dim3((unsigned)(p.nkb * bh)), dim3(kThreads), 0, a.stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nqb > 0) {
+    hipLaunchKernelGGL((dq_kernel<E, D, MASK>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0, a.stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <typename E, int D>
+hipError_t launch_m(const BwdArgs& a) {
+  switch (a.g.mask_kind()) {
+    case kMaskNone: return launch<E, D, kMaskNone>(a);
+    case kMaskUpper: return launch<E, D, kMaskUpper>(a);
+    default: return launch<E, D, kMaskBand>(a);
+  }
+}
+
+template <typename E>
+hipError_t launch_d(const BwdArgs& a) {
+  return a.g.d == 64 ? launch_m<E, 64>(a) : launch_m<E, 128>(a);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(long long bh, int nq) {
+  return (size_t)bh * (size_t)((nq + kTile - 1) / kTile * kTile) * 8;
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs& a) {
+  return a.dtype == kDtypeF16 ? launch_d<F16>(a) : launch_d<Bf16>(a);
+}
+
+}  // namespace fa

@@ -32,6 +32,40 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Element types of the 16-bit paths. Tiles and MFMA operands travel as
+// 16-byte vectors typed bf16x8 whatever the element type (loads, LDS and
+// lane exchanges only move bits); the matrix instruction and the conversions
+// to and from fp32 are the only places where the type matters.
+struct Bf16 {
+  __device__ __forceinline__ static f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) { return mfma32(a, b, c); }
+  // fp32 -> element, round to nearest even
+  __device__ __forceinline__ static __bf16 cvt(float x) { return (__bf16)x; }
+  // element -> fp32 from the low / high half of a 32-bit word
+  __device__ __forceinline__ static float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  __device__ __forceinline__ static float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+};
+
+struct F16 {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  __device__ __forceinline__ static f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  __device__ __forceinline__ static __bf16 cvt(float x) { return __builtin_bit_cast(__bf16, (_Float16)x); }
+  __device__ __forceinline__ static float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  __device__ __forceinline__ static float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  }
+};
+
+// two fp32 -> two elements packed low | high << 16, round to nearest even
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, E::cvt(a)) | ((uint32_t)__builtin_bit_cast(uint16_t, E::cvt(b)) << 16);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // max / sum of x over the lane pair (l, l ^ 32)
@@ -213,39 +247,54 @@ struct TileCopy {
 };
 
 // Direct global -> LDS tile copy (buffer_load ... lds, 16 bytes per lane).
-// A ROWS x D bf16 tile is THREADS/64 waves x kInstr instructions; instruction
-// i of wave w fills LDS bytes [(w * kInstr + i) * 1024, +1024) of the tile, lane
-// l writing 16 bytes at +16 l. Each lane therefore fetches the global chunk
-// that the swizzled layout stores at its LDS position. Rows past the end of
-// the buffer resource (num_records) arrive as zeros, so ragged tails need no
-// branches. No registers hold the tile.
+// A ROWS x D tile of 16-bit elements is THREADS/64 waves x kInstr
+// instructions; instruction i of wave w fills LDS bytes [(w * kInstr + i) *
+// 1024, +1024) of the tile, lane l writing 16 bytes at +16 l, i.e. rows
+// lrow + i * kRowsPerInstr of the tile. Each lane fetches the global chunk
+// that the swizzled layout stores at its LDS position. Global rows are
+// `stride` bytes apart (a multiple of 16, at least one row): the lane's part
+// of the offset is lrow * stride plus its swizzled chunk, the rest is a
+// wave-uniform row offset. Rows past the end of the buffer resource (see
+// rows_rsrc) arrive as zeros, so ragged tails need no branches. No registers
+// hold the tile.
 template <int ROWS, int D, int THREADS>
 struct TileDma {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileBytes = ROWS * kRowBytes;
   static constexpr int kWaves = THREADS / 64;
   static constexpr int kInstr = kTileBytes / 1024 / kWaves;
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;
   static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into whole 1 KB wave copies");
-  uint32_t lane_off[kInstr];  // byte offset of this lane's chunk inside a global tile
-  int lds_off;                // byte offset of this wave's first 1 KB inside an LDS tile
+  static_assert(1024 % kRowBytes == 0, "a 1 KB wave copy must hold whole rows");
+  // the swizzle depends on row % 16 only, so the chunk offsets repeat after
+  // kPeriod instructions
+  static constexpr int kPeriod = kInstr < 16 / kRowsPerInstr ? kInstr : 16 / kRowsPerInstr;
+  uint32_t chunk_off[kPeriod];  // byte offset of this lane's (swizzled) chunk inside its row
+  uint32_t lrow;                // this lane's row in the wave's first instruction
+  int lds_off;                  // byte offset of this wave's first 1 KB inside an LDS tile
 
   __device__ __forceinline__ void init(int wave, int lane) {
     lds_off = wave * kInstr * 1024;
+    lrow = (uint32_t)((lds_off + 16 * lane) / kRowBytes);
+    const int chunk = ((16 * lane) % kRowBytes) / 16;
 #pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int pos = lds_off + i * 1024 + 16 * lane;  // LDS byte position in the tile
-      const int row = pos / kRowBytes;
-      const int chunk = (pos % kRowBytes) / 16;
-      lane_off[i] = (uint32_t)(row * kRowBytes + Swz<D>::chunk(row, chunk) * 16);
-    }
+    for (int i = 0; i < kPeriod; ++i) chunk_off[i] = (uint32_t)(Swz<D>::chunk(lrow + i * kRowsPerInstr, chunk) * 16);
   }
-  // Copy rows [row0, row0 + ROWS) of the tensor behind `rsrc` into `tile`.
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0) const {
-    const uint32_t base = (uint32_t)row0 * kRowBytes;
+  // Copy rows [row0, row0 + ROWS) of the tensor behind `rsrc` (rows `stride`
+  // bytes apart) into `tile`. The whole offset goes in the vector offset: the
+  // buffer range check that zero-fills rows past the end does not include the
+  // scalar offset.
+  // The stride is laundered through an empty asm so the compiler computes
+  // the offsets here, per copy, instead of hoisting kInstr loop-invariant
+  // offsets per tensor into registers for the whole loop.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0, uint32_t stride) const {
+    asm volatile("" : "+s"(stride));
+    const uint32_t lane_base = (lrow + (uint32_t)row0) * stride;
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
       FA_LDS void* dst = (FA_LDS void*)((FA_LDS char*)(FA_LDS bf16_t*)tile + lds_off + i * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, base + lane_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, lane_base + chunk_off[i % kPeriod] + i * kRowsPerInstr * stride, 0,
+                                               0, 0);
     }
   }
 };
@@ -253,6 +302,14 @@ struct TileDma {
 // Buffer resource over `bytes` bytes at `base`; loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer resource over `rows` rows of D 16-bit elements, `stride` bytes
+// apart: it ends right after the last element of the last row, so a 16-byte
+// load of any row at or past `rows` lies wholly outside and returns zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, uint32_t stride) {
+  return make_rsrc(base, rows > 0 ? (uint32_t)(rows - 1) * stride + D * 2 : 0u);
 }
 
 // Wait until every vector-memory operation of this wave (including the

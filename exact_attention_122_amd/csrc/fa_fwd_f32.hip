@@ -6,7 +6,8 @@
 // exp(m_old - m_new) whenever m grows; after the last tile O = acc / l and
 // LSE = m + ln l. Here one thread owns one query row and the dot products run
 // on plain fp32 FMAs: this kernel serves small fp32 problems, where latency,
-// not throughput, sets the time.
+// not throughput, sets the time. Shapes, strides and band masks follow the
+// same rules as the 16-bit kernels.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -22,44 +23,62 @@ struct F32Params {
   const float* v;
   float* o;
   float* lse;
-  int n;
+  long long q_sb, q_sh, q_sr, k_sb, k_sh, k_sr, v_sb, v_sh, v_sr, o_sb, o_sh, o_sr;  // strides (elements)
+  int heads;
+  int nq, nk;
+  int diag;         // nk - nq: the key aligned with query 0
+  int wl, wr;       // band (banded kernels only), both >= 0
   int nqb;
   float c;          // |scale| * log2(e)
   float scale_abs;
   float qsign;      // -1 when scale < 0 (exact sign flip of Q), else +1
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(F32Params p) {
   __shared__ float k_lds[kKeys][D];
   __shared__ float v_lds[kKeys][D];
   const int tid = threadIdx.x;
-  const int n = p.n;
+  const int nq = p.nq, nk = p.nk;
   const int head = blockIdx.x / p.nqb;
   const int qblk = blockIdx.x - head * p.nqb;
-  const size_t head_off = (size_t)head * n * D;
-  const int qi = qblk * kRows + tid;
+  const int hb = head / p.heads, hh = head - hb * p.heads;
+  const float* qh = p.q + hb * p.q_sb + hh * p.q_sh;
+  const float* kh = p.k + hb * p.k_sb + hh * p.k_sh;
+  const float* vh = p.v + hb * p.v_sb + hh * p.v_sh;
+  const int q_row0 = qblk * kRows;
+  const int qi = q_row0 + tid;
 
   float q[D], acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    q[e] = qi < n ? p.q[head_off + (size_t)qi * D + e] * p.qsign : 0.f;
+    q[e] = qi < nq ? qh[qi * p.q_sr + e] * p.qsign : 0.f;
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  // live keys of this row: [lo, hi]
+  const int lo = BAND ? qi + p.diag - p.wl : 0;
+  const int hi = BAND ? min(qi + p.diag + p.wr, nk - 1) : nk - 1;
 
-  const int q_last = min(n, qblk * kRows + kRows) - 1;
-  const int n_tiles = CAUSAL ? q_last / kKeys + 1 : (n + kKeys - 1) / kKeys;
+  // key tiles of this work-group's band
+  const int q_last = min(nq, q_row0 + kRows) - 1;
+  int key_base = 0, n_tiles = (nk + kKeys - 1) / kKeys;
+  if (BAND) {
+    const int k_lo = max(0, q_row0 + p.diag - p.wl);
+    const int k_hi = min(nk - 1, q_last + p.diag + p.wr);
+    key_base = k_lo / kKeys * kKeys;
+    n_tiles = k_hi < k_lo ? 0 : (k_hi - key_base) / kKeys + 1;
+  }
   for (int j = 0; j < n_tiles; ++j) {
-    const int key0 = j * kKeys;
+    const int key0 = key_base + j * kKeys;
     __syncthreads();
     for (int e = tid; e < kKeys * D / 4; e += kRows) {
       const int row = e / (D / 4);
       const int c4 = e % (D / 4);
       float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-      if (key0 + row < n) {
-        kx = *(const float4*)(p.k + head_off + (size_t)(key0 + row) * D + 4 * c4);
-        vx = *(const float4*)(p.v + head_off + (size_t)(key0 + row) * D + 4 * c4);
+      if (key0 + row < nk) {
+        kx = *(const float4*)(kh + (key0 + row) * p.k_sr + 4 * c4);
+        vx = *(const float4*)(vh + (key0 + row) * p.v_sr + 4 * c4);
       }
       *(float4*)&k_lds[row][4 * c4] = kx;
       *(float4*)&v_lds[row][4 * c4] = vx;
@@ -74,7 +93,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(F32Params p) {
 #pragma unroll
       for (int e = 0; e < D; ++e) dot = fmaf(q[e], k_lds[kk][e], dot);
       const int key = key0 + kk;
-      const bool dead = key >= n || (CAUSAL && key > qi);
+      const bool dead = key > hi || key < lo;
       s[kk] = dead ? -INFINITY : dot;
       mx = fmaxf(mx, s[kk]);
     }
@@ -94,17 +113,17 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(F32Params p) {
     m = mnew;
   }
 
-  if (qi < n) {
+  if (qi < nq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* orow = p.o + head_off + (size_t)qi * D;
+    float* orow = p.o + hb * p.o_sb + hh * p.o_sh + qi * p.o_sr;
 #pragma unroll
     for (int e = 0; e < D; e += 4)
       *(float4*)(orow + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
-    p.lse[(size_t)head * n + qi] = l > 0.f ? m * p.scale_abs + logf(l) : -INFINITY;
+    p.lse[(long long)head * nq + qi] = l > 0.f ? m * p.scale_abs + logf(l) : -INFINITY;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 hipError_t launch(const FwdArgs& a) {
   F32Params p;
   p.q = (const float*)a.q;
@@ -112,22 +131,32 @@ hipError_t launch(const FwdArgs& a) {
   p.v = (const float*)a.v;
   p.o = (float*)a.o;
   p.lse = a.lse;
-  p.n = a.n;
-  p.nqb = (a.n + kRows - 1) / kRows;
+  p.q_sb = a.sq.b, p.q_sh = a.sq.h, p.q_sr = a.sq.r;
+  p.k_sb = a.sk.b, p.k_sh = a.sk.h, p.k_sr = a.sk.r;
+  p.v_sb = a.sv.b, p.v_sh = a.sv.h, p.v_sr = a.sv.r;
+  p.o_sb = a.so.b, p.o_sh = a.so.h, p.o_sr = a.so.r;
+  p.heads = a.g.heads;
+  p.nq = a.g.nq;
+  p.nk = a.g.nk;
+  p.diag = a.g.nk - a.g.nq;
+  p.wl = a.g.wl < 0 ? a.g.nq + a.g.nk : a.g.wl;
+  p.wr = a.g.wr < 0 ? a.g.nq + a.g.nk : a.g.wr;
+  p.nqb = (a.g.nq + kRows - 1) / kRows;
   p.scale_abs = fabsf(a.scale);
   p.c = p.scale_abs * kLog2e;
   p.qsign = a.scale < 0.f ? -1.f : 1.f;
-  const long long blocks = (long long)p.nqb * a.bh;
+  const long long blocks = (long long)p.nqb * a.g.batch * a.g.heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kRows), 0, a.stream, p);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, BAND>), dim3((unsigned)blocks), dim3(kRows), 0, a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  const bool band = a.g.banded();
+  if (a.g.d == 64) return band ? launch<64, true>(a) : launch<64, false>(a);
+  return band ? launch<128, true>(a) : launch<128, false>(a);
 }
 
 }  // namespace fa

@@ -1,4 +1,4 @@
-// Forward attention, bf16 in / bf16 out, fp32 accumulation, MFMA on gfx950.
+// Forward attention, bf16 or fp16 in and out, fp32 accumulation, MFMA on gfx950.
 //
 // Method ('FlashAttention', josueisai.com, section on the softmax trick; the
 // kerneldigest.dev glossary entry): a work-group owns a block of query rows of
@@ -37,6 +37,15 @@
 //    8 / c (a factor 2^8 in the exponentials); otherwise the stale m is kept.
 //    O / l and m + ln l do not depend on the reference point, so the result is
 //    the same up to rounding while most tiles skip the O rescale entirely.
+//  * Shapes and masks: queries and keys may differ in number (query i is
+//    aligned with key i + nk - nq, so new queries attend over a cache of
+//    earlier keys) and a band mask keeps, for each query, the keys from wl
+//    before to wr after its aligned key (causal: wr = 0; a sliding window:
+//    wl = w). A work-group visits only the K/V tiles its band touches; tiles
+//    that straddle a band edge or the end of the keys mask dead scores to
+//    -inf. A row that sees no key ends with l = 0: O = 0 and LSE = -inf.
+//  * Tensors are addressed through per-tensor batch, head and row strides
+//    (d contiguous), so views of other layouts need no copy.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -59,7 +68,12 @@ struct FwdParams {
   const bf16_t* v;
   bf16_t* o;
   float* lse;
-  int n;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch / head strides (elements)
+  int q_sr, k_sr, v_sr, o_sr;                                // row strides (elements)
+  int heads;
+  int nq, nk;
+  int diag;      // nk - nq: the key aligned with query 0
+  int wl, wr;    // band (banded kernels only), both >= 0
   int nqb;       // query blocks per head
   int nblocks;   // work-groups in the grid
   float c;       // |scale| * log2(e)
@@ -83,12 +97,12 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
 // O += P_{j-1} V_{j-1}
-template <int D, int KB>
+template <typename E, int D, int KB>
 __device__ __forceinline__ void pv_mfma(RowState<D, KB>& st, const bf16_t* vt, const TrRead<D>& vrd) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int t = 0; t < 2 * KB; ++t) st.acc[db] = mfma32(vrd(vt, t, db), st.pb[t], st.acc[db]);
+    for (int t = 0; t < 2 * KB; ++t) st.acc[db] = E::mfma(vrd(vt, t, db), st.pb[t], st.acc[db]);
 }
 
 // Matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.
@@ -96,18 +110,18 @@ __device__ __forceinline__ void pv_mfma(RowState<D, KB>& st, const bf16_t* vt, c
 // operands are already in flight, so the matrix core does not wait on LDS
 // latency (the other wave on the SIMD is in its softmax phase and cannot
 // cover it).
-template <int D, int KB>
+template <typename E, int D, int KB>
 __device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* kt, const bf16_t* vt,
                                              const RowRead<D>& krd, const TrRead<D>& vrd,
                                              const bf16x8 (&qf)[D / 16]) {
-  pv_mfma<D, KB>(st, vt, vrd);
+  pv_mfma<E, D, KB>(st, vt, vrd);
   f32x16 s[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b) s[b] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-    for (int b = 0; b < KB; ++b) s[b] = mfma32(krd(kt, b, ks), qf[ks], s[b]);
+    for (int b = 0; b < KB; ++b) s[b] = E::mfma(krd(kt, b, ks), qf[ks], s[b]);
 #pragma unroll
   for (int b = 0; b < KB; ++b) {
     st.s[b] = s[b];
@@ -131,9 +145,9 @@ __device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* 
   for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
 }
 
-// Softmax phase for the tile whose scores are in st.s. `masked` tiles
-// (causal diagonal, ragged end) set the scores of dead keys to -inf first.
-template <int D, int KB, bool CAUSAL>
+// Softmax phase for the tile whose scores are in st.s. `masked` tiles (band
+// edges, ragged end) set the scores of dead keys to -inf first.
+template <typename E, int D, int KB, int MASK>
 __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
                                               bool masked) {
   constexpr int kN = 16 * KB;  // scores per lane
@@ -144,13 +158,15 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[16 * b + r] = st.s[b][r];
   if (masked) {
-    const int lim = CAUSAL ? min(qi, p.n - 1) : p.n - 1;  // last live key of this row
+    // live keys of this row: [lo, hi]
+    const int hi = MASK != kMaskNone ? min(qi + p.diag + p.wr, p.nk - 1) : p.nk - 1;
+    const int lo = MASK == kMaskBand ? qi + p.diag - p.wl : 0;
     const int k0 = key0 + 4 * hw;
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int b = i >> 4, r = i & 15;
       const int kr = k0 + 32 * b + 8 * (r >> 2) + (r & 3);
-      x[i] = kr > lim ? -INFINITY : x[i];
+      x[i] = (kr > hi || (MASK == kMaskBand && kr < lo)) ? -INFINITY : x[i];
     }
   }
   // Running max: in-lane as a tree, then across the half-wave pair. The
@@ -203,22 +219,23 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 #pragma unroll
   for (int t = 0; t < 2 * KB; ++t)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.pb[t][e] = (__bf16)x[8 * t + e];
+    for (int e = 0; e < 8; ++e) st.pb[t][e] = E::cvt(x[8 * t + e]);
 #pragma unroll
   for (int t = 0; t < 2 * KB; ++t) fence_regs(st.pb[t]);
   fence_regs(st.l);
 }
 
-// One iteration j < n_tiles of the main loop: group A copies set j + 1
-// (K_{j+1} into `kn`, V_j into `vn`), then matrix(j) on set j (K_j in `kt`,
-// V_{j-1} in `vt`), a barrier, softmax(j), the wait for this wave's copies and
-// a barrier. The buffers are fixed per call (the loop is unrolled by two) so
-// the compiler can see that reading set j never depends on the copy into the
-// other set. Every wave runs every tile of its work-group: a tile wholly past
-// a wave's last causal key has all scores at -inf, so its p are 0 and it
-// changes nothing.
-template <int D, int KB, bool CAUSAL>
-__device__ __forceinline__ void fwd_iteration(int j, int n_tiles, bool group_b, const bf16_t* kt, const bf16_t* vt,
+// One iteration j < n_tiles of the main loop (keys key_base + j * kBlockN
+// onwards): group A copies set j + 1 (K_{j+1} into `kn`, V_j into `vn`), then
+// matrix(j) on set j (K_j in `kt`, V_{j-1} in `vt`), a barrier, softmax(j),
+// the wait for this wave's copies and a barrier. The buffers are fixed per
+// call (the loop is unrolled by two) so the compiler can see that reading set
+// j never depends on the copy into the other set. Every wave runs every tile
+// of its work-group: a tile wholly outside a wave's band has all scores at
+// -inf, so its p are 0 and it changes nothing.
+template <typename E, int D, int KB, int MASK>
+__device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, bool group_b, const bf16_t* kt,
+                                              const bf16_t* vt,
                                               bf16_t* kn, bf16_t* vn,
                                               const TileDma<32 * KB, D, kThreads / 2>& dma,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
@@ -226,15 +243,19 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, bool group_b, 
                                               const bf16x8 (&qf)[D / 16], RowState<D, KB>& st, const FwdParams& p,
                                               int wq0, int qi, int lane) {
   constexpr int kBlockN = 32 * KB;
+  const int key0 = key_base + j * kBlockN;
   if (!group_b) {
-    if (j + 1 < n_tiles) dma.issue(krs, kn, (j + 1) * kBlockN);
-    dma.issue(vrs, vn, j * kBlockN);
+    if (j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
+    dma.issue(vrs, vn, key0, 2u * p.v_sr);
   }
-  matrix_phase<D, KB>(st, kt, vt, krd, vrd, qf);
+  matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
   __syncthreads();
-  const int key0 = j * kBlockN;
-  const bool masked = (key0 + kBlockN > p.n) || (CAUSAL && key0 + kBlockN - 1 > wq0);
-  softmax_phase<D, KB, CAUSAL>(st, p, key0, qi, lane, masked);
+  // the wave's rows are wq0 .. wq0 + 31: the last has the highest lower
+  // bound, the first the lowest upper bound
+  const bool masked = (key0 + kBlockN > p.nk) ||
+                      (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
+                      (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
+  softmax_phase<E, D, KB, MASK>(st, p, key0, qi, lane, masked);
   wait_vmem();
   __syncthreads();
 }
@@ -246,8 +267,9 @@ constexpr int fwd_blocks_per_cu() {
   return D <= 64 ? 2 : 1;
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_kernel(FwdParams p) {
+template <typename E, int D, int MASK>
+__global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(FwdParams p) {
+  constexpr bool BAND = MASK != kMaskNone;
   constexpr int KB = key_blocks<D>();
   constexpr int kBlockN = 32 * KB;  // keys per tile
   // Two sets of (K tile, V tile), declared as separate objects so the compiler
@@ -262,42 +284,52 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_ker
   const bool group_b = wave >= kWaves / 2;
   const int hw = lane >> 5;
   const int col = lane & 31;
-  const int n = p.n;
+  const int nq = p.nq, nk = p.nk;
 
   const int logical = xcd_logical_block(blockIdx.x, p.nblocks);
-  const int head = logical / p.nqb;
+  const int head = logical / p.nqb;  // b * heads + h
   int qblk = logical - head * p.nqb;
-  if (CAUSAL) qblk = p.nqb - 1 - qblk;  // longest rows first
-  const size_t head_off = (size_t)head * n * D;
+  if (BAND) qblk = p.nqb - 1 - qblk;  // longest rows first under a causal band
+  const int hb = head / p.heads, hh = head - hb * p.heads;
+  const bf16_t* qh = p.q + hb * p.q_sb + hh * p.q_sh;
+  const bf16_t* kh = p.k + hb * p.k_sb + hh * p.k_sh;
+  const bf16_t* vh = p.v + hb * p.v_sb + hh * p.v_sh;
   const int q_row0 = qblk * kBlockM;
   const int wq0 = q_row0 + wave * 32;
   const int qi = wq0 + col;
 
+  // K/V tiles of this work-group's band: [key_base, key_base + n_tiles * kBlockN)
+  const int q_last = min(nq, q_row0 + kBlockM) - 1;
+  int key_base = 0, n_tiles = (nk + kBlockN - 1) / kBlockN;
+  if (BAND) {
+    const int k_lo = max(0, q_row0 + p.diag - p.wl);
+    const int k_hi = min(nk - 1, q_last + p.diag + p.wr);
+    key_base = k_lo / kBlockN * kBlockN;
+    n_tiles = k_hi < k_lo ? 0 : (k_hi - key_base) / kBlockN + 1;
+  }
+
   // K/V tiles stream straight into LDS. Group A copies every tile (see the
   // loop below); start the first K tile before loading Q.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)n * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)n * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc<D>(kh, nk, 2u * p.k_sr);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc<D>(vh, nk, 2u * p.v_sr);
   TileDma<kBlockN, D, kThreads / 2> dma;
   dma.init(wave & (kWaves / 2 - 1), lane);
   RowRead<D> krd;
   krd.init(lane);
   TrRead<D> vrd;
   vrd.init(lane);
-  if (!group_b) dma.issue(krs, k_lds0, 0);
+  if (!group_b) dma.issue(krs, k_lds0, key_base, 2u * p.k_sr);
 
   bf16x8 qf[D / 16];
   {
-    const bf16_t* qrow = p.q + head_off + (size_t)qi * D + 8 * hw;
+    const bf16_t* qrow = qh + (long long)qi * p.q_sr + 8 * hw;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (qi < n) x = *(const u32x4*)(qrow + 16 * ks);
+      if (qi < nq) x = *(const u32x4*)(qrow + 16 * ks);
       qf[ks] = __builtin_bit_cast(bf16x8, x ^ p.qsign);
     }
   }
-
-  const int q_last = min(n, q_row0 + kBlockM) - 1;
-  const int n_tiles = CAUSAL ? (q_last / kBlockN + 1) : (n + kBlockN - 1) / kBlockN;
 
   RowState<D, KB> st;
 #pragma unroll
@@ -322,42 +354,48 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_bf16_ker
   if (group_b) __syncthreads();
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
-    fwd_iteration<D, KB, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
-                             wq0, qi, lane);
-    fwd_iteration<D, KB, CAUSAL>(j + 1, n_tiles, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, krd, vrd, qf, st,
-                             p, wq0, qi, lane);
+    fwd_iteration<E, D, KB, MASK>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+                                  vrd, qf, st, p, wq0, qi, lane);
+    fwd_iteration<E, D, KB, MASK>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs,
+                                  krd, vrd, qf, st, p, wq0, qi, lane);
   }
   if (j < n_tiles)
-    fwd_iteration<D, KB, CAUSAL>(j, n_tiles, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd, vrd, qf, st, p,
-                             wq0, qi, lane);
+    fwd_iteration<E, D, KB, MASK>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+                                  vrd, qf, st, p, wq0, qi, lane);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
-  pv_mfma<D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
+  pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) __syncthreads();
 
-  // epilogue: O = acc / l, LSE = m * |scale| + ln l
+  // epilogue: O = acc / l, LSE = m * |scale| + ln l (-inf for a row with no key)
   const float lt = pair_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qi < n) {
-    bf16_t* orow = p.o + head_off + (size_t)qi * D;
+  if (qi < nq) {
+    bf16_t* orow = p.o + hb * p.o_sb + hh * p.o_sh + (long long)qi * p.o_sr;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 w;
-        w.x = pack_bf16x2(st.acc[db][4 * g] * inv, st.acc[db][4 * g + 1] * inv);
-        w.y = pack_bf16x2(st.acc[db][4 * g + 2] * inv, st.acc[db][4 * g + 3] * inv);
+        w.x = pack2<E>(st.acc[db][4 * g] * inv, st.acc[db][4 * g + 1] * inv);
+        w.y = pack2<E>(st.acc[db][4 * g + 2] * inv, st.acc[db][4 * g + 3] * inv);
         *(uint2*)(orow + db * 32 + 8 * g + 4 * hw) = w;
       }
-    if (hw == 0) p.lse[(size_t)head * n + qi] = lt > 0.f ? st.m * p.scale_abs + __logf(lt) : -INFINITY;
+    if (hw == 0) p.lse[(long long)head * nq + qi] = lt > 0.f ? st.m * p.scale_abs + __logf(lt) : -INFINITY;
   }
 }
 
-template __global__ void fwd_bf16_kernel<64, false>(FwdParams);
-template __global__ void fwd_bf16_kernel<64, true>(FwdParams);
-template __global__ void fwd_bf16_kernel<128, false>(FwdParams);
-template __global__ void fwd_bf16_kernel<128, true>(FwdParams);
+#define FA_FWD_INSTANCES(E)                                        \
+  template __global__ void fwd_kernel<E, 64, kMaskNone>(FwdParams);   \
+  template __global__ void fwd_kernel<E, 64, kMaskUpper>(FwdParams);  \
+  template __global__ void fwd_kernel<E, 64, kMaskBand>(FwdParams);   \
+  template __global__ void fwd_kernel<E, 128, kMaskNone>(FwdParams);  \
+  template __global__ void fwd_kernel<E, 128, kMaskUpper>(FwdParams); \
+  template __global__ void fwd_kernel<E, 128, kMaskBand>(FwdParams);
+FA_FWD_INSTANCES(Bf16)
+FA_FWD_INSTANCES(F16)
+#undef FA_FWD_INSTANCES
 
-template <int D, bool CAUSAL>
+template <typename E, int D, int MASK>
 hipError_t launch(const FwdArgs& a) {
   FwdParams p;
   p.q = (const bf16_t*)a.q;
@@ -365,9 +403,19 @@ hipError_t launch(const FwdArgs& a) {
   p.v = (const bf16_t*)a.v;
   p.o = (bf16_t*)a.o;
   p.lse = a.lse;
-  p.n = a.n;
-  p.nqb = (a.n + kBlockM - 1) / kBlockM;
-  p.nblocks = p.nqb * a.bh;
+  p.q_sb = a.sq.b, p.q_sh = a.sq.h, p.q_sr = (int)a.sq.r;
+  p.k_sb = a.sk.b, p.k_sh = a.sk.h, p.k_sr = (int)a.sk.r;
+  p.v_sb = a.sv.b, p.v_sh = a.sv.h, p.v_sr = (int)a.sv.r;
+  p.o_sb = a.so.b, p.o_sh = a.so.h, p.o_sr = (int)a.so.r;
+  p.heads = a.g.heads;
+  p.nq = a.g.nq;
+  p.nk = a.g.nk;
+  p.diag = a.g.nk - a.g.nq;
+  // an absent bound becomes one no key can reach
+  p.wl = a.g.wl < 0 ? a.g.nq + a.g.nk : a.g.wl;
+  p.wr = a.g.wr < 0 ? a.g.nq + a.g.nk : a.g.wr;
+  p.nqb = (a.g.nq + kBlockM - 1) / kBlockM;
+  p.nblocks = p.nqb * a.g.batch * a.g.heads;
   p.scale_abs = fabsf(a.scale);
   // c is kept strictly positive: with scale = 0 every exp2(c (s - m)) still
   // rounds to exactly 1 (uniform weights) while exp2(c * -inf) stays 0 for
@@ -375,15 +423,28 @@ hipError_t launch(const FwdArgs& a) {
   p.c = fmaxf(p.scale_abs * kLog2e, 1e-30f);
   p.thr = p.scale_abs > 0.f ? 8.f / p.c : 3.0e38f;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.nblocks), dim3(kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<E, D, MASK>), dim3(p.nblocks), dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_m(const FwdArgs& a) {
+  switch (a.g.mask_kind()) {
+    case kMaskNone: return launch<E, D, kMaskNone>(a);
+    case kMaskUpper: return launch<E, D, kMaskUpper>(a);
+    default: return launch<E, D, kMaskBand>(a);
+  }
+}
+
+template <typename E>
+hipError_t launch_d(const FwdArgs& a) {
+  return a.g.d == 64 ? launch_m<E, 64>(a) : launch_m<E, 128>(a);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+hipError_t launch_fwd_mfma(const FwdArgs& a) {
+  return a.dtype == kDtypeF16 ? launch_d<F16>(a) : launch_d<Bf16>(a);
 }
 
 }  // namespace fa

@@ -22,9 +22,11 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_BF16 = 0
 FA_FP32 = 1
+FA_FP16 = 2
 
 EXPORTS = ("fa_version", "fa_status_string", "fa_last_error_detail", "fa_fwd",
-           "fa_bwd_workspace_bytes", "fa_bwd")
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex_workspace_bytes",
+           "fa_bwd_ex")
 
 _lib = None
 
@@ -52,6 +54,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    lp = ctypes.POINTER(ctypes.c_longlong)
+    lib.fa_fwd_ex.restype = i
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, lp, lp, lp, lp, f, i, i, i, vp]
+    lib.fa_bwd_ex_workspace_bytes.restype = sz
+    lib.fa_bwd_ex_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                              lp, lp, lp, lp, lp, lp, lp, lp, f, i, i, i, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -83,7 +93,9 @@ def _dtype_code(t) -> int:
         return FA_BF16
     if t.dtype == torch.float32:
         return FA_FP32
-    raise RuntimeError(f"dtype {t.dtype} is not built (bfloat16 or float32)")
+    if t.dtype == torch.float16:
+        return FA_FP16
+    raise RuntimeError(f"dtype {t.dtype} is not built (bfloat16, float16 or float32)")
 
 
 def _shape(q):
@@ -160,4 +172,107 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None
                                dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
                                workspace.data_ptr(), workspace.numel(), _stream(q))
     _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+# ---------------------------------------------- general shapes and masks ---
+
+def _band(causal: bool, window):
+    """(window_left, window_right) for the C call; -1 = no bound."""
+    left, right = (-1, -1) if window is None else (
+        -1 if window[0] is None else int(window[0]), -1 if window[1] is None else int(window[1]))
+    if causal:
+        if right not in (-1, 0):
+            raise RuntimeError("causal sets window_right = 0; window gives another right bound")
+        right = 0
+    return left, right
+
+
+def _strides(t, name):
+    """{batch, head, row} element strides of a [B, H, rows, d] view (d contiguous)."""
+    if t.dim() != 4:
+        raise RuntimeError(f"{name}: expected a [B, H, rows, d] tensor, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1 and t.shape[3] != 1:
+        raise RuntimeError(f"{name}: the last dimension (d) must be contiguous")
+    return (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ex_operands(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise RuntimeError("expected [B, H, rows, d] tensors")
+    B, H, Nq, d = (int(x) for x in q.shape)
+    Nk = int(k.shape[2])
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise RuntimeError("K and V must be [B, H, Nk, d] with Q's B, H and d")
+    for t in (k, v):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise RuntimeError("Q, K and V must share dtype and device")
+    if not q.is_cuda:
+        raise RuntimeError("tensors must live in GPU memory")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_ex(q, k, v, causal: bool = False, window=None, scale: float | None = None,
+              out=None, lse=None):
+    """O, LSE for Nq queries over Nk keys with a band mask and strided views.
+
+    ``window`` = (left, right) bounds the visible keys around each query's
+    aligned key i + Nk - Nq (None = unbounded); ``causal`` sets right = 0.
+    Any [B, H, rows, d] views with d contiguous are accepted (see include/fa.h).
+    """
+    import torch
+    B, H, Nq, Nk, d = _ex_operands(q, k, v)
+    left, right = _band(causal, window)
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, Nq, d) or out.dtype != q.dtype or out.device != q.device:
+        raise RuntimeError("out must be [B, H, Nq, d] of Q's dtype and device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise RuntimeError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    st = load_library().fa_fwd_ex(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+        _strides(q, "Q"), _strides(k, "K"), _strides(v, "V"), _strides(out, "O"),
+        float(scale), left, right, _dtype_code(q), _stream(q))
+    _check(st, "fa_fwd_ex")
+    return out, lse
+
+
+def fa_bwd_ex_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: int = FA_BF16) -> int:
+    return int(load_library().fa_bwd_ex_workspace_bytes(B, H, Nq, Nk, d, dtype))
+
+
+def fa_bwd_ex(q, k, v, o, do, lse, causal: bool = False, window=None, scale: float | None = None,
+              dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV for O, LSE = fa_fwd_ex(q, k, v, causal, window, scale)."""
+    import torch
+    B, H, Nq, Nk, d = _ex_operands(q, k, v)
+    left, right = _band(causal, window)
+    if scale is None:
+        scale = default_scale(d)
+    for t, shape, name in ((o, (B, H, Nq, d), "O"), (do, (B, H, Nq, d), "dO")):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or t.device != q.device:
+            raise RuntimeError(f"{name} must be [B, H, Nq, d] of Q's dtype and device")
+    dq = torch.empty((B, H, Nq, d), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((B, H, Nk, d), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, Nk, d), dtype=q.dtype, device=q.device) if dv is None else dv
+    for t, shape, name in ((dq, (B, H, Nq, d), "dQ"), (dk, (B, H, Nk, d), "dK"), (dv, (B, H, Nk, d), "dV")):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or t.device != q.device:
+            raise RuntimeError(f"{name} has the wrong shape, dtype or device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise RuntimeError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    code = _dtype_code(q)
+    need = fa_bwd_ex_workspace_bytes(B, H, Nq, Nk, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_bwd_ex(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
+        _strides(q, "Q"), _strides(k, "K"), _strides(v, "V"), _strides(o, "O"), _strides(do, "dO"),
+        _strides(dq, "dQ"), _strides(dk, "dK"), _strides(dv, "dV"),
+        float(scale), left, right, code, workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "fa_bwd_ex")
     return dq, dk, dv

@@ -9,9 +9,10 @@ Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
   each tensor is ``standard_normal(size=(B, H, N, d), dtype=float32)``;
   for bf16 workloads the fp32 draw is rounded to bfloat16 with
   round-to-nearest-even on the bit pattern (the same rule as
-  ``torch.Tensor.to(torch.bfloat16)``).
-Layout: contiguous [B, H, N, d], d innermost. bf16 tensors are carried as
-their uint16 bit patterns.
+  ``torch.Tensor.to(torch.bfloat16)``); fp16 workloads round it to IEEE half
+  (numpy's float32 -> float16 cast, also round-to-nearest-even).
+Layout: contiguous [B, H, N, d], d innermost (K and V may have their own
+row count Nk). bf16 tensors are carried as their uint16 bit patterns.
 
 The workloads mirror the pages' long-context self-attention (score matrices
 of tens of millions of entries per head, 'FlashAttention' on josueisai.com,
@@ -36,6 +37,23 @@ WORKLOADS = {
                                    causal=True, backward=False, seed=1224),
     "train_n4096_d128": dict(B=2, H=16, N=4096, d=128, dtype="bf16",
                              causal=False, backward=True, seed=1225),
+    # General shapes and masks (beyond equal-length, top-left causal
+    # self-attention), each at a long-context size:
+    #   a local window of 1024 earlier keys over 16k tokens;
+    "window_n16384_d128_w1024": dict(B=2, H=32, N=16384, d=128, dtype="bf16",
+                                     causal=False, window=(1024, 0),
+                                     backward=True, seed=1226),
+    #   512 new queries per head over a 16k-key cache, causal (aligned with
+    #   the last keys);
+    "prefill_q512_k16384_d128": dict(B=8, H=32, N=512, nk=16384, d=128,
+                                     dtype="bf16", causal=True,
+                                     backward=True, seed=1227),
+    #   the 8k self-attention shape in fp16, and in [B, N, H, d] memory.
+    "fp16_n8192_d128": dict(B=1, H=32, N=8192, d=128, dtype="fp16",
+                            causal=False, backward=True, seed=1228),
+    "bnhd_n8192_d128": dict(B=1, H=32, N=8192, d=128, dtype="bf16",
+                            causal=False, backward=True, layout="bnhd",
+                            seed=1229),
 }
 
 
@@ -61,8 +79,8 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 @dataclass
 class Tensor:
     """A host tensor as the GPU will see it: raw storage plus its dtype."""
-    storage: np.ndarray          # uint16 bits (bf16) or float32 values
-    dtype: str                   # "bf16" | "fp32"
+    storage: np.ndarray          # uint16 bits (bf16), float16 or float32 values
+    dtype: str                   # "bf16" | "fp16" | "fp32"
     sha256: str = field(default="")
 
     def __post_init__(self):
@@ -90,32 +108,40 @@ class Tensor:
             t = torch.from_numpy(self.storage.copy())
         return t.to(device)
 
+    @staticmethod
+    def from_f32(x: np.ndarray, dtype: str) -> "Tensor":
+        """Round float32 values to the storage type (round-to-nearest-even)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if dtype == "bf16":
+            return Tensor(f32_to_bf16_bits(x), "bf16")
+        if dtype == "fp16":
+            return Tensor(x.astype(np.float16), "fp16")
+        if dtype == "fp32":
+            return Tensor(x, "fp32")
+        raise ValueError(f"unknown dtype {dtype!r}")
+
 
 def _draw(rng: np.random.Generator, shape, dtype: str) -> Tensor:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if dtype == "bf16":
-        return Tensor(f32_to_bf16_bits(x), "bf16")
-    if dtype == "fp32":
-        return Tensor(x, "fp32")
-    raise ValueError(f"unknown dtype {dtype!r}")
+    return Tensor.from_f32(rng.standard_normal(size=shape, dtype=np.float32), dtype)
 
 
 def generate(B: int, H: int, N: int, d: int, dtype: str, seed: int,
-             with_grad_output: bool = False) -> dict:
-    """Draw Q, K, V (and dO) of shape [B, H, N, d] from one seeded PCG64."""
+             with_grad_output: bool = False, nk: int | None = None) -> dict:
+    """Draw Q [B, H, N, d], K and V [B, H, nk, d] (nk = N by default) and dO
+    [B, H, N, d] from one seeded PCG64, in that order."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    shape = (B, H, N, d)
-    out = {"q": _draw(rng, shape, dtype), "k": _draw(rng, shape, dtype),
-           "v": _draw(rng, shape, dtype)}
+    nk = N if nk is None else nk
+    out = {"q": _draw(rng, (B, H, N, d), dtype), "k": _draw(rng, (B, H, nk, d), dtype),
+           "v": _draw(rng, (B, H, nk, d), dtype)}
     if with_grad_output:
-        out["do"] = _draw(rng, shape, dtype)
+        out["do"] = _draw(rng, (B, H, N, d), dtype)
     return out
 
 
 def generate_workload(name: str) -> dict:
     w = WORKLOADS[name]
     return generate(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"],
-                    with_grad_output=w["backward"])
+                    with_grad_output=w["backward"], nk=w.get("nk"))
 
 
 def default_scale(d: int) -> float:

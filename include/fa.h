@@ -12,20 +12,31 @@
  * section on recomputing instead of remembering).
  *
  * Conventions shared by every entry point:
- *  - Tensors are dense, contiguous [B, H, N, d] with d innermost. Q, K, V, O,
- *    dO, dQ, dK and dV all have the element type `dtype`; LSE is always
- *    float32 [B, H, N] and holds the natural-log log-sum-exp of the scaled
- *    scores of each query row.
+ *  - Tensors are [B, H, rows, d] with d innermost. fa_fwd and fa_bwd take them
+ *    dense and contiguous with N rows each; fa_fwd_ex and fa_bwd_ex take Nq
+ *    query rows (Q, O, dO, dQ) and Nk key rows (K, V, dK, dV) and, per
+ *    tensor, three element strides {batch, head, row} (NULL = contiguous).
+ *    Q, K, V, O, dO, dQ, dK and dV all have the element type `dtype`; LSE is
+ *    always contiguous float32 [B, H, Nq] and holds the natural-log
+ *    log-sum-exp of the scaled scores of each query row.
  *  - Every tensor pointer is a DEVICE pointer (memory of the current HIP
  *    device). Base pointers must be 16-byte aligned. The caller allocates and
  *    owns every buffer; the library allocates, frees and retains nothing.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; outputs are valid once the stream reaches that point and
  *    inputs must stay unchanged until then.
- *  - causal = 1 masks key j for query i whenever j > i (top-left alignment,
- *    equal query and key lengths). Tiles that are wholly masked are skipped.
- *  - B, H or N equal to 0 is an empty problem: nothing is enqueued and FA_OK
- *    is returned.
+ *  - Masks. Query i is aligned with key i + Nk - Nq (the queries are the last
+ *    Nq positions of the key sequence, as when new tokens attend over a cache
+ *    of earlier keys). The _ex calls take a band: key j is visible to query i
+ *    iff  i + Nk - Nq - window_left <= j <= i + Nk - Nq + window_right,  a
+ *    bound of -1 being absent. causal = 1 in fa_fwd / fa_bwd is the band
+ *    (-1, 0): key j is masked for query i whenever j > i. A sliding window of
+ *    w earlier keys is (w, 0) (local attention, which josueisai.com's
+ *    'FlashAttention' page, section on what you gain and what not, pairs with
+ *    the method for very long sequences). Tiles wholly outside the band are
+ *    skipped. A query row that sees no key gets O = 0, LSE = -inf and dQ = 0.
+ *  - A problem with no query row (B, H or Nq equal to 0) is empty: nothing is
+ *    enqueued and FA_OK is returned. With Nk = 0 every row sees no key.
  *  - Errors are returned as fa_status; no exception crosses the ABI. A
  *    request the kernels do not cover returns FA_ERR_UNSUPPORTED; there is
  *    never a silent fallback to a different implementation. After an error,
@@ -50,7 +61,9 @@ typedef enum fa_status {
 
 typedef enum fa_dtype {
   FA_BF16 = 0, /* bfloat16 storage, float32 accumulation */
-  FA_FP32 = 1  /* float32 storage and arithmetic (no reduced-precision modes) */
+  FA_FP32 = 1, /* float32 storage and arithmetic (no reduced-precision modes) */
+  FA_FP16 = 2  /* IEEE half storage, float32 accumulation (foqum.io's FAQ on
+                  FlashAttention names FP16 and BF16 as the formats it runs in) */
 } fa_dtype;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -74,7 +87,7 @@ const char* fa_last_error_detail(void);
  *  LSE      out  [B, H, N] float32
  *  scale    any finite float (1/sqrt(d) in the usual use)
  *  d        64 or 128
- *  dtype    FA_BF16 or FA_FP32
+ *  dtype    FA_BF16, FA_FP16 or FA_FP32
  * O and LSE must not overlap any input.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -103,13 +116,69 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  *  dQ, dK, dV      out  [B, H, N, d] of `dtype`
  *  workspace       device scratch of at least fa_bwd_workspace_bytes() bytes,
  *                  16-byte aligned, owned by the caller
- *  d               64 or 128;  dtype FA_BF16 only (FA_FP32 -> UNSUPPORTED)
+ *  d               64 or 128;  dtype FA_BF16 or FA_FP16 (FA_FP32 -> UNSUPPORTED)
  * Outputs and the workspace must not overlap any input or each other.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd for general shapes, layouts and masks: Nq queries over Nk keys, a
+ * band mask (window_left, window_right; -1 = no bound; (-1, -1) = no mask,
+ * (-1, 0) = causal, (w, 0) = sliding window), and strided operands. Same
+ * definition as fa_fwd otherwise (josueisai.com 'FlashAttention', sections on
+ * the matrix that should never be stored and on the softmax trick).
+ *
+ *  Q, O     [B, H, Nq, d];  K, V  [B, H, Nk, d];  LSE out, contiguous [B, H, Nq]
+ *  *_strides  NULL for contiguous, else 3 int64 element strides {batch, head,
+ *             row}; d is contiguous (stride 1). Strides must be >= 0, the row
+ *             stride >= d, every stride a multiple of 16 bytes (8 elements in
+ *             16-bit types, 4 in fp32), and one head's rows must span < 2 GiB;
+ *             otherwise FA_ERR_UNSUPPORTED. O's layout must give every element
+ *             its own address (FA_ERR_INVALID_ARGUMENT otherwise). Inputs may
+ *             share memory (e.g. one packed QKV tensor, or a batch or head
+ *             stride of 0 to broadcast K and V).
+ *  window_left, window_right  -1 or >= 0 (FA_ERR_INVALID_ARGUMENT otherwise)
+ * The address range of O (lowest to highest element) and LSE must not overlap
+ * any input's.
+ */
+int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+              int B, int H, int Nq, int Nk, int d,
+              const long long* q_strides, const long long* k_strides,
+              const long long* v_strides, const long long* o_strides,
+              float scale, int window_left, int window_right, int dtype,
+              void* stream);
+
+/*
+ * Bytes of workspace fa_bwd_ex needs: B*H*ceil(Nq/64)*64*8 (two float32 per
+ * query row); 0 for an empty problem or arguments fa_bwd_ex would reject.
+ */
+size_t fa_bwd_ex_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+
+/*
+ * fa_bwd for general shapes, layouts and masks, with the conventions of
+ * fa_fwd_ex. O and LSE are what fa_fwd_ex wrote for the same Q, K, V, band and
+ * scale. Key rows that no query sees get dK = dV = 0; query rows that see no
+ * key get dQ = 0.
+ *
+ *  Q, O, dO, dQ  [B, H, Nq, d];  K, V, dK, dV  [B, H, Nk, d]
+ *  strides       as fa_fwd_ex, one set per tensor; dQ, dK, dV must each give
+ *                every element its own address
+ *  dtype         FA_BF16 or FA_FP16 (FA_FP32 -> UNSUPPORTED)
+ * The address ranges of dQ, dK, dV and the workspace must not overlap any
+ * input's, LSE's or each other's (separate gradient buffers).
+ */
+int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
+              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+              int B, int H, int Nq, int Nk, int d,
+              const long long* q_strides, const long long* k_strides,
+              const long long* v_strides, const long long* o_strides,
+              const long long* do_strides, const long long* dq_strides,
+              const long long* dk_strides, const long long* dv_strides,
+              float scale, int window_left, int window_right, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -9,6 +9,10 @@ from exact_attention_122_amd import fa, inputs
 TOL = {
     "bf16": dict(o=2e-2, lse=1e-3, grad=2e-2),
     "fp32": dict(o=1e-5, lse=1e-5, grad=None),
+    # fp16 keeps 11 significant bits to bf16's 8: the same rounding steps (P,
+    # dS and the outputs) err 8x less, so the bf16 bounds shrink 4x for O and
+    # 2x for the gradients, keeping a 2-4x margin; LSE is fp32 in both.
+    "fp16": dict(o=5e-3, lse=1e-3, grad=1e-2),
 }
 # Relative Frobenius bound on top of max-abs. The max-abs bound alone is loose
 # for outputs whose entries are ~1/sqrt(N); bf16 rounding of P and of the
@@ -29,6 +33,11 @@ def compare(name, got, ref, atol, rel=None):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    # rows with no visible key: the oracle's LSE is -inf and so must ours be
+    dead = np.isneginf(ref)
+    if dead.any():
+        assert np.all(np.isneginf(got[dead])), f"{name}: expected -inf where no key is visible"
+        got, ref = got[~dead], ref[~dead]
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     err = float(np.abs(got - ref).max()) if got.size else 0.0
     assert err <= atol, f"{name}: max abs err {err:.3e} > {atol:.1e}"

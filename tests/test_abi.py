@@ -87,7 +87,7 @@ def test_fwd_empty_problem_is_a_no_op(kw):
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16 only"),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED, "not built"),
     (dict(ws=0), fa.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
     (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARGUMENT, "smaller"),
@@ -112,6 +112,11 @@ def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP32) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP16) == 64 * 8
+    # general shapes: statistics are per query row
+    assert fa.fa_bwd_ex_workspace_bytes(2, 4, 100, 7000, 128) == 2 * 4 * 128 * 8
+    assert fa.fa_bwd_ex_workspace_bytes(2, 4, 0, 7000, 128) == 0
+    assert fa.fa_bwd_ex_workspace_bytes(1, 1, 64, 0, 64, fa.FA_FP16) == 64 * 8
 
 
 def test_binding_refuses_cpu_tensors():
@@ -134,3 +139,77 @@ def _load_fresh(path):
         return fa.load_library(path)
     finally:
         fa._lib = saved
+
+
+# ------------------------------------------------ general-shape entry points ---
+
+def _ll(*xs):
+    return (ctypes.c_longlong * 3)(*xs)
+
+
+def fwd_ex(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=128, Nk=256, d=64,
+           qs=None, ks=None, vs=None, os_=None, scale=0.125, wl=-1, wr=-1, dtype=fa.FA_BF16):
+    lib = fa.load_library()
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, qs, ks, vs, os_, scale, wl, wr, dtype, None)
+
+
+def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, scale=0.125, wl=-1, wr=-1,
+           dtype=fa.FA_BF16, ws=P[9], ws_bytes=1 << 20):
+    lib = fa.load_library()
+    ptrs = ptrs or P[:9]
+    strides = strides or [None] * 8
+    return lib.fa_bwd_ex(*ptrs, B, H, Nq, Nk, d, *strides, scale, wl, wr, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k=0), fa.FA_ERR_INVALID_ARGUMENT, "K is NULL"),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
+    (dict(wl=-2), fa.FA_ERR_INVALID_ARGUMENT, "window"),
+    (dict(wr=-7), fa.FA_ERR_INVALID_ARGUMENT, "window"),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(qs=_ll(2 * 128 * 64, 128 * 64, 60)), fa.FA_ERR_UNSUPPORTED, "below d"),
+    (dict(ks=_ll(2 * 256 * 64, 256 * 64, 68)), fa.FA_ERR_UNSUPPORTED, "multiples of 8"),
+    (dict(vs=_ll(-1, 256 * 64, 64)), fa.FA_ERR_UNSUPPORTED, "negative"),
+    (dict(dtype=fa.FA_FP32, qs=_ll(2 * 128 * 64, 128 * 64, 66)), fa.FA_ERR_UNSUPPORTED, "multiples of 4"),
+    # O's heads share memory: two elements at one address
+    (dict(os_=_ll(128 * 64, 0, 64)), fa.FA_ERR_INVALID_ARGUMENT, "one address"),
+    (dict(os_=_ll(128 * 64, 64, 64)), fa.FA_ERR_INVALID_ARGUMENT, "one address"),
+    (dict(o=P[1]), fa.FA_ERR_INVALID_ARGUMENT, "O overlaps K"),
+    (dict(Nk=1 << 20, ks=_ll(0, 0, 1024)), fa.FA_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(Nq=(1 << 28) + 1), fa.FA_ERR_UNSUPPORTED, "2^28"),
+])
+def test_fwd_ex_rejects_on_the_host(kw, status, needle):
+    assert fwd_ex(**kw) == status
+    assert needle in fa.fa_last_error_detail()
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(B=0), dict(Nq=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_fwd_ex_empty_problem_is_a_no_op(kw):
+    assert fwd_ex(**kw) == fa.FA_OK
+    assert fa.fa_last_error_detail() == ""
+
+
+def test_fwd_ex_inputs_may_share_memory():
+    # packed QKV [B, N, 3, H, d] views and a broadcast K/V (head stride 0) pass
+    # the host checks; O is still required to be disjoint. The call is made
+    # with fake pointers, so it must stop before any launch: an empty B.
+    qkv = _ll(128 * 3 * 2 * 64, 64, 3 * 2 * 64)
+    assert fwd_ex(B=0, q=P[0], k=P[0] + 128, v=P[0] + 256, Nk=128, qs=qkv, ks=qkv, vs=qkv) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16 only"),
+    (dict(ws_bytes=8), fa.FA_ERR_INVALID_ARGUMENT, "smaller"),
+    (dict(wl=-3), fa.FA_ERR_INVALID_ARGUMENT, "window"),
+    (dict(ptrs=P[:6] + [P[7]] + P[7:9]), fa.FA_ERR_INVALID_ARGUMENT, "dQ overlaps dK"),
+    (dict(strides=[None] * 5 + [_ll(2 * 128 * 64, 0, 64)] + [None] * 2), fa.FA_ERR_INVALID_ARGUMENT, "one address"),
+    (dict(strides=[None] * 4 + [_ll(2 * 128 * 64, 128 * 64, 40)] + [None] * 3), fa.FA_ERR_UNSUPPORTED, "below d"),
+])
+def test_bwd_ex_rejects_on_the_host(kw, status, needle):
+    assert bwd_ex(**kw) == status
+    assert needle in fa.fa_last_error_detail()
+
+
+def test_bwd_ex_empty_problem_is_a_no_op():
+    assert bwd_ex(Nq=0, Nk=0, ptrs=[0] * 9, ws=0, ws_bytes=0) == fa.FA_OK
+    assert bwd_ex(B=0, ptrs=[0] * 9, ws=0, ws_bytes=0) == fa.FA_OK

@@ -121,3 +121,78 @@ def test_causal_bwd_n16384_d128_heads():
     compare("dQ", f64(dq)[0, 1], rq, TOL["bf16"]["grad"], REL_FRO)
     compare("dK", f64(dk)[0, 1], rk, TOL["bf16"]["grad"], REL_FRO)
     compare("dV", f64(dv)[0, 1], rv, TOL["bf16"]["grad"], REL_FRO)
+
+
+# ----------------------------------------------- general-shape workloads ---
+# The workloads bench.py --suite times, in the same calls (fa_fwd_ex /
+# fa_bwd_ex with the same layouts); sampled rows and whole heads against the
+# oracle.
+
+def _suite_run(name):
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate_workload(name)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (g[x].to_torch(dev) for x in ("q", "k", "v", "do"))
+    if w.get("layout") == "bnhd":
+        q, k, v, do = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v, do))
+    window = w.get("window", (-1, 0) if w["causal"] else (-1, -1))
+    scale = inputs.default_scale(w["d"])
+    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale)
+    torch.cuda.synchronize()
+    win = tuple(None if x < 0 else x for x in window)
+    return w, g, scale, win, (o, lse, dq, dk, dv)
+
+
+def _check_suite(name, heads_fwd, heads_bwd):
+    w, g, scale, win, (o, lse, dq, dk, dv) = _suite_run(name)
+    dtype = w["dtype"]
+    rng = np.random.default_rng(w["seed"])
+    o64, l64 = f64(o), f64(lse)
+    gq, gk, gv = f64(dq), f64(dk), f64(dv)
+    q64, k64, v64, do64 = (g[x].to_f64() for x in ("q", "k", "v", "do"))
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(gq)) and np.all(np.isfinite(gk))
+    for flat in heads_fwd:
+        b, h = divmod(flat, w["H"])
+        rows = _sample_rows(w["N"], rng)
+        ro, rl = oracle.forward_head(q64[b, h], k64[b, h], v64[b, h], scale, rows=rows, window=win)
+        compare(f"O[{b},{h}]", o64[b, h, rows], ro, TOL[dtype]["o"], REL_FRO)
+        compare(f"LSE[{b},{h}]", l64[b, h, rows], rl, TOL[dtype]["lse"])
+    for flat in heads_bwd:
+        b, h = divmod(flat, w["H"])
+        rq, rk, rv = oracle.backward_head(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, window=win)
+        for nm, got, ref in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
+            compare(f"{nm}[{b},{h}]", got[b, h], ref, TOL[dtype]["grad"] * max(1.0, float(np.abs(ref).max())),
+                    REL_FRO)
+    return o, lse, (dq, dk, dv)
+
+
+def test_window_n16384_w1024_sampled():
+    _check_suite("window_n16384_d128_w1024", heads_fwd=[0, 45], heads_bwd=[63])
+
+
+def test_prefill_q512_k16384_sampled():
+    _check_suite("prefill_q512_k16384_d128", heads_fwd=[0, 100, 255], heads_bwd=[7, 200])
+
+
+def test_fp16_n8192_sampled():
+    _check_suite("fp16_n8192_d128", heads_fwd=[0, 31], heads_bwd=[5])
+
+
+def test_bnhd_n8192_equals_contiguous_bitwise():
+    """Same kernels, same order of operations: the [B, N, H, d] layout gives
+    exactly the contiguous results, which the other tests check."""
+    w, g, scale, win, outs = _suite_run("bnhd_n8192_d128")
+    dev = torch.device("cuda:0")
+    q, k, v, do = (g[x].to_torch(dev) for x in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_ex(q, k, v, scale=scale)
+    grads = fa.fa_bwd_ex(q, k, v, o, do, lse, scale=scale)
+    torch.cuda.synchronize()
+    for a, b in zip(outs, (o, lse) + tuple(grads)):
+        assert torch.equal(a, b)
+    rng = np.random.default_rng(w["seed"])
+    rows = _sample_rows(w["N"], rng)
+    ro, rl = oracle.forward_head(g["q"].to_f64()[0, 9], g["k"].to_f64()[0, 9], g["v"].to_f64()[0, 9], scale,
+                                 rows=rows)
+    compare("O", f64(o)[0, 9, rows], ro, TOL["bf16"]["o"], REL_FRO)
+    compare("LSE", f64(lse)[0, 9, rows], rl, TOL["bf16"]["lse"])

@@ -53,3 +53,21 @@ def test_workload_table():
     assert inputs.WORKLOADS["train_n4096_d128"]["backward"]
     assert inputs.default_scale(64) == 0.125
     assert inputs.default_scale(128) == float(np.float32(1 / np.sqrt(128)))
+
+
+def test_fp16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    g = inputs.generate(1, 2, 40, 16, "fp16", 9)
+    x = np.random.Generator(np.random.PCG64(9)).standard_normal(size=(1, 2, 40, 16), dtype=np.float32)
+    ref = torch.from_numpy(x).to(torch.float16).numpy()
+    np.testing.assert_array_equal(g["q"].storage, ref)
+    t = g["q"].to_torch()
+    assert t.dtype == torch.float16
+    np.testing.assert_array_equal(t.float().numpy(), g["q"].to_f32())
+
+
+def test_unequal_key_length_keeps_the_draw_order():
+    g = inputs.generate(1, 1, 5, 8, "fp32", 11, with_grad_output=True, nk=7)
+    rng = np.random.Generator(np.random.PCG64(11))
+    for name, rows in (("q", 5), ("k", 7), ("v", 7), ("do", 5)):
+        np.testing.assert_array_equal(g[name].storage, rng.standard_normal(size=(1, 1, rows, 8), dtype=np.float32))
