@@ -11,7 +11,8 @@ FLOPs follow the attention convention: forward 4*N^2*d per head (halved under
 causal masking), backward 2.5x that. Prints ONE JSON line.
 
 `--suite` instead times the general-shape workloads (a sliding window, new
-queries over a long key cache, fp16, a [B, N, H, d] layout) through
+queries over a long key cache, fp16, a [B, N, H, d] layout, head dimensions
+32, 96 and 256) through
 fa_fwd_ex / fa_bwd_ex and prints one JSON line per workload; there FLOPs are
 4*d per visible (query, key) pair, counted exactly for the mask.
 """
@@ -97,7 +98,8 @@ def visible_pairs(nq, nk, window):
     return int(np.maximum(0, hi - lo + 1).sum())
 
 
-SUITE = ("window_n16384_d128_w1024", "prefill_q512_k16384_d128", "fp16_n8192_d128", "bnhd_n8192_d128")
+SUITE = ("window_n16384_d128_w1024", "prefill_q512_k16384_d128", "fp16_n8192_d128", "bnhd_n8192_d128",
+         "d32_n8192", "d96_n8192", "d256_n8192")
 
 
 def run_suite(args):

@@ -59,7 +59,10 @@ int check_dims(int B, int H, int nq, int nk, int d, int dtype, Problem* pr) {
   if (d <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head dimension d=%d must be positive", d);
   if (dtype != FA_BF16 && dtype != FA_FP32 && dtype != FA_FP16)
     return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d is not built (64 or 128)", d);
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d is not built (32, 64, 96, 128 or 256)", d);
+  if (dtype == FA_FP32 && d > 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d is not built for fp32 (at most 128)", d);
   const long long bh = (long long)B * H;
   if (bh > INT_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "B*H=%lld exceeds INT_MAX", bh);
   const long long n = std::max(nq, nk);

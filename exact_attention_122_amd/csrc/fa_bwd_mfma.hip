@@ -70,14 +70,21 @@ __device__ __forceinline__ const bf16_t* head_base(const bf16_t* t, long long sb
   return t + b * sb + (head - b * heads) * sh;
 }
 
-// One thread group of D/8 lanes per padded query row: D_i = dO_i . O_i and
-// LSE_i * log2(e). A row that saw no key (LSE = -inf) stores +inf, so the
+// Lanes per query row in row_stats_kernel: D / 8 chunks of 8 elements,
+// rounded up to a power of two for the shuffle reduction.
+template <int D>
+constexpr int row_lanes() {
+  return D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32;
+}
+
+// One group of row_lanes<D>() lanes per padded query row: D_i = dO_i . O_i
+// and LSE_i * log2(e). A row that saw no key (LSE = -inf) stores +inf, so the
 // kernels' exp2(c s - L) is 0 for it on every key.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(const bf16_t* o, const bf16_t* dout, const float* lse,
                                                              float* stats, Strides so, Strides sdo, int heads, int nq,
                                                              int nq_pad, long long padded_rows) {
-  constexpr int kLanesPerRow = D / 8;
+  constexpr int kLanesPerRow = row_lanes<D>();
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long prow = gid / kLanesPerRow;
   const int part = (int)(gid % kLanesPerRow);
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const bf16_t* o, co
   const int r = (int)(prow - (long long)head * nq_pad);
   const bool valid = prow < padded_rows && r < nq;
   float acc = 0.f;
-  if (valid) {
+  if (valid && part < D / 8) {
     const int b = head / heads, h = head - b * heads;
     const u32x4 x = *(const u32x4*)(o + b * so.b + h * so.h + r * so.r + part * 8);
     const u32x4 y = *(const u32x4*)(dout + b * sdo.b + h * sdo.h + r * sdo.r + part * 8);
@@ -216,10 +223,11 @@ __device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur
 
 template <typename E, int D, int MASK>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t q_lds1[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t d_lds0[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t d_lds1[kTile * D];
+  constexpr int P = lds_pitch<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds1[kTile * P];
   __shared__ __attribute__((aligned(16))) float s_lds0[2 * kTile];
   __shared__ __attribute__((aligned(16))) float s_lds1[2 * kTile];
 
@@ -380,13 +388,21 @@ __device__ __forceinline__ void dq_step(int j, int n_tiles, int key_base, const 
   __syncthreads();
 }
 
+// dQ work-groups per CU: two, except at d = 256, whose Q, dO and dQ rows fill
+// the registers of one wave per SIMD and whose K/V tiles fill the LDS.
+template <int D>
+constexpr int dq_blocks_per_cu() {
+  return D >= 256 ? 1 : 2;
+}
+
 template <typename E, int D, int MASK>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(BwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kTile * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kTile * D];
+  constexpr int P = lds_pitch<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kTile * P];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -500,10 +516,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
   template __global__ void dq_kernel<E, D, kMaskBand>(BwdParams);                                         \
   template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
                                                   Strides, int, int, int, long long);
-FA_BWD_INSTANCES(Bf16, 64)
-FA_BWD_INSTANCES(Bf16, 128)
-FA_BWD_INSTANCES(F16, 64)
-FA_BWD_INSTANCES(F16, 128)
+#define FA_BWD_INSTANCES_D(E) \
+  FA_BWD_INSTANCES(E, 32)     \
+  FA_BWD_INSTANCES(E, 64)     \
+  FA_BWD_INSTANCES(E, 96)     \
+  FA_BWD_INSTANCES(E, 128)    \
+  FA_BWD_INSTANCES(E, 256)
+FA_BWD_INSTANCES_D(Bf16)
+FA_BWD_INSTANCES_D(F16)
+#undef FA_BWD_INSTANCES_D
 #undef FA_BWD_INSTANCES
 
 template <typename E, int D, int MASK>
@@ -543,7 +564,7 @@ hipError_t launch(const BwdArgs& a) {
   // no work; with no key, dQ = 0 and dkdv has none
   const long long padded_rows = bh * p.nq_pad;
   if (padded_rows > 0) {
-    const long long stat_blocks = (padded_rows * (D / 8) + kThreads - 1) / kThreads;
+    const long long stat_blocks = (padded_rows * row_lanes<D>() + kThreads - 1) / kThreads;
     hipLaunchKernelGGL((row_stats_kernel<E, D>), dim3((unsigned)stat_blocks), dim3(kThreads), 0, a.stream,
                        (const bf16_t*)a.o, p.dout, a.lse, a.workspace, a.so, a.sdo, g.heads, g.nq, p.nq_pad,
                        padded_rows);
@@ -573,7 +594,13 @@ hipError_t launch_m(const BwdArgs& a) {
 
 template <typename E>
 hipError_t launch_d(const BwdArgs& a) {
-  return a.g.d == 64 ? launch_m<E, 64>(a) : launch_m<E, 128>(a);
+  switch (a.g.d) {
+    case 32: return launch_m<E, 32>(a);
+    case 64: return launch_m<E, 64>(a);
+    case 96: return launch_m<E, 96>(a);
+    case 128: return launch_m<E, 128>(a);
+    default: return launch_m<E, 256>(a);
+  }
 }
 
 }  // namespace

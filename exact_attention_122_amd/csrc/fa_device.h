@@ -94,102 +94,83 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Round-to-nearest-even float -> bf16, packed pairwise (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e];
-  return r;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
 // ---------------------------------------------------------------------------
-// LDS tiles of ROWS x D bf16, row-major, 16-byte chunks XOR-swizzled per row so
-// that both read patterns below are free of bank conflicts. gfx950's LDS has
-// 64 banks of 4 bytes, so one cycle serves 16 slots of 16 bytes; slot =
-// (row * D / 8 + physical chunk) mod 16.
+// LDS tiles of ROWS x D 16-bit elements, row-major with a row pitch of P =
+// lds_pitch<D>() elements, 16-byte chunks XOR-swizzled per row so that both
+// read patterns below are free of bank conflicts. gfx950's LDS has 64 banks
+// of 4 bytes, so one cycle serves 16 slots of 16 bytes; slot = (row * P / 8 +
+// physical chunk) mod 16.
 //   * row-operand reads (ds_read_b128): 16 lanes per cycle read 16
 //     consecutive rows at one logical chunk c; they need 16 distinct slots.
 //   * transposed reads (ds_read_b64_tr_b16): 32 lanes per cycle read 4
 //     consecutive rows (aligned to 4) x 4 consecutive chunks (aligned to 4);
 //     they need 16 distinct slots.
 // physical chunk = c ^ f(row), with f depending on row % 16:
-//   D = 128 (16 chunks, slot = chunk): f = 4 (row % 4) + (row / 4) % 4 is a
-//     permutation of 0..15 (row reads), and 4 aligned rows get distinct
-//     f / 4, i.e. distinct aligned groups of 4 chunks (transposed reads).
-//   D = 64 (8 chunks, slot = 8 (row % 2) + chunk): f = 4 ((row / 2) % 2) +
+//   16 or more chunks per row (slot = chunk mod 16): f = 4 (row % 4) +
+//     (row / 4) % 4 is a permutation of 0..15 (row reads), and 4 aligned rows
+//     get distinct f / 4, i.e. distinct aligned groups of 4 chunks
+//     (transposed reads).
+//   8 chunks (slot = 8 (row % 2) + chunk): f = 4 ((row / 2) % 2) +
 //     (row / 4) % 4 is a permutation of 0..7 over the even rows and over the
 //     odd rows of any 16, and rows r, r + 2 of an aligned group of 4 get
 //     distinct f / 4.
+//   4 chunks (slot = 4 (row % 4) + chunk): f = (row / 4) % 4 separates the
+//     four rows of any 16 that share row % 4; 4 aligned rows already differ
+//     in row % 4.
+// D = 96 has 12 chunks, which no XOR pattern keeps in range, so its rows are
+// padded to 128 elements and use the 16-chunk pattern (the 4 spare chunks of
+// each row hold zeros and are never read).
 // ---------------------------------------------------------------------------
 template <int D>
+constexpr int lds_pitch() {
+  return D == 96 ? 128 : D;
+}
+
+template <int P>
 struct Swz {
-  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  static constexpr int kChunks = P / 8;  // 16-byte chunks per row
+  static_assert(kChunks == 4 || kChunks == 8 || kChunks >= 16, "no swizzle for this row pitch");
   __device__ __forceinline__ static int chunk(int row, int c) {
     if constexpr (kChunks >= 16) {
       return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
-    } else {
+    } else if constexpr (kChunks == 8) {
       return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+    } else {
+      return c ^ ((row >> 2) & 3);
     }
   }
   // element offset of (row, col) for a col that is a multiple of 4
   __device__ __forceinline__ static int offset(int row, int col) {
-    return row * D + (chunk(row, col >> 3) << 3) + (col & 7);
+    return row * P + (chunk(row, col >> 3) << 3) + (col & 7);
   }
 };
-
-// A/B operand of 8 consecutive elements of one row, columns [c8*8, c8*8+8).
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row8(const bf16_t* tile, int row, int c8) {
-  const FA_LDS bf16x8* p =
-      (const FA_LDS bf16x8*)((const FA_LDS bf16_t*)tile + row * D + (Swz<D>::chunk(row, c8) << 3));
-  return *p;
-}
-
-// Transposed operand: with rows r0 + 4 * half-wave + {0..3} (read 0) and
-// r0 + 8 + 4 * half-wave + {0..3} (read 1), lane l receives column
-// c0 + (l % 32) of those 8 rows, i.e. a 32x16 A operand whose k index runs
-// over rows in the order the score accumulators hold them.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_tr8(const bf16_t* tile, int r0, int c0, int lane) {
-  const int s = lane & 15;
-  const int hw = lane >> 5;
-  const int col = c0 + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
-  const int row_a = r0 + 4 * hw + (s >> 2);
-  const int row_b = row_a + 8;
-  const FA_LDS bf16_t* base = (const FA_LDS bf16_t*)tile;
-  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + Swz<D>::offset(row_a, col)));
-  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + Swz<D>::offset(row_b, col)));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  return __builtin_bit_cast(bf16x8, z);
-}
 
 // Per-lane byte offsets of the two LDS read patterns, computed once per kernel
 // so the reads in the loop need no address arithmetic (tile base and constant
 // row offsets fold into the instruction's immediate offset).
 //  RowRead: A/B operand of 8 consecutive elements of row (lane % 32) + 32 kb,
 //           columns [16 ks + 8 hw, +8).
-//  TrRead:  the transposed operand of lds_tr8 at rows 16 t, columns 32 db.
+//  TrRead:  the transposed operand at rows 16 t + 4 hw + {0..3, 8..11} and
+//           column 32 db + lane % 32: with read 0 at rows +{0..3} and read 1
+//           at rows +{8..11}, lane l receives a 32x16 A operand whose k index
+//           runs over rows in the order the score accumulators hold them.
 template <int D>
 struct RowRead {
+  static constexpr int P = lds_pitch<D>();
   uint32_t off[D / 16];
   __device__ __forceinline__ void init(int lane) {
     const int row = lane & 31, hw = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(row * D + (Swz<D>::chunk(row, 2 * ks + hw) << 3)) * 2;
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(row * P + (Swz<P>::chunk(row, 2 * ks + hw) << 3)) * 2;
   }
   __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int kb, int ks) const {
-    return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks] + kb * 32 * D * 2);
+    return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks] + kb * 32 * P * 2);
   }
 };
 
 template <int D>
 struct TrRead {
+  static constexpr int P = lds_pitch<D>();
   uint32_t off[D / 32][2];
   __device__ __forceinline__ void init(int lane) {
     const int s = lane & 15, hw = lane >> 5;
@@ -199,50 +180,17 @@ struct TrRead {
       for (int i = 0; i < 2; ++i) {
         const int row = 4 * hw + (s >> 2) + 8 * i;
         const int col = 32 * db + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
-        off[db][i] = (uint32_t)Swz<D>::offset(row, col) * 2;
+        off[db][i] = (uint32_t)Swz<P>::offset(row, col) * 2;
       }
   }
   // rows t * 16 + ... (f(row) only depends on row % 16, so +16 rows is a constant)
   __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int t, int db) const {
-    const FA_LDS char* base = (const FA_LDS char*)(const FA_LDS bf16_t*)tile + t * 16 * D * 2;
+    const FA_LDS char* base = (const FA_LDS char*)(const FA_LDS bf16_t*)tile + t * 16 * P * 2;
     i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][0]));
     i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][1]));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8, z);
-  }
-};
-
-// Cooperative tile copy global -> registers -> LDS. ROWS x D bf16, rows at
-// or beyond `valid_rows` are filled with zeros.
-template <int ROWS, int D, int THREADS>
-struct TileCopy {
-  static constexpr int kChunks = ROWS * D / 8;
-  static constexpr int kPerThread = kChunks / THREADS;
-  static_assert(kChunks % THREADS == 0, "tile must split evenly over threads");
-  u32x4 r[kPerThread];
-
-  __device__ __forceinline__ void load(const bf16_t* src, int valid_rows, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * THREADS;
-      const int row = c / (D / 8);
-      const int ch = c % (D / 8);
-      if (row < valid_rows) {
-        r[i] = *(const u32x4*)(src + (size_t)row * D + ch * 8);
-      } else {
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * THREADS;
-      const int row = c / (D / 8);
-      const int ch = c % (D / 8);
-      *(FA_LDS u32x4*)((FA_LDS bf16_t*)tile + row * D + (Swz<D>::chunk(row, ch) << 3)) = r[i];
-    }
   }
 };
 
@@ -259,7 +207,8 @@ struct TileCopy {
 // hold the tile.
 template <int ROWS, int D, int THREADS>
 struct TileDma {
-  static constexpr int kRowBytes = D * 2;
+  static constexpr int P = lds_pitch<D>();
+  static constexpr int kRowBytes = P * 2;  // in LDS
   static constexpr int kTileBytes = ROWS * kRowBytes;
   static constexpr int kWaves = THREADS / 64;
   static constexpr int kInstr = kTileBytes / 1024 / kWaves;
@@ -278,7 +227,13 @@ struct TileDma {
     lrow = (uint32_t)((lds_off + 16 * lane) / kRowBytes);
     const int chunk = ((16 * lane) % kRowBytes) / 16;
 #pragma unroll
-    for (int i = 0; i < kPeriod; ++i) chunk_off[i] = (uint32_t)(Swz<D>::chunk(lrow + i * kRowsPerInstr, chunk) * 16);
+    for (int i = 0; i < kPeriod; ++i) {
+      // the global chunk this LDS position holds; padding chunks of a padded
+      // row point past every buffer (offsets stay below 2^31 + 2^31), so they
+      // are filled with zeros
+      const int g = Swz<P>::chunk(lrow + i * kRowsPerInstr, chunk);
+      chunk_off[i] = g < D / 8 ? (uint32_t)(g * 16) : 0x80000000u;
+    }
   }
   // Copy rows [row0, row0 + ROWS) of the tensor behind `rsrc` (rows `stride`
   // bytes apart) into `tile`. The whole offset goes in the vector offset: the

@@ -56,10 +56,12 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per work-group
 
-// 32-key blocks per K/V tile
+// 32-key blocks per K/V tile: 128 keys where the registers allow long
+// phases, 64 at small d (two work-groups per CU share the registers), 32 at
+// d = 256 (the O accumulators alone take half the registers)
 template <int D>
 constexpr int key_blocks() {
-  return D >= 128 ? 4 : 2;
+  return D >= 256 ? 1 : D >= 96 ? 4 : 2;
 }
 
 struct FwdParams {
@@ -260,8 +262,8 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   __syncthreads();
 }
 
-// d = 64 needs few enough registers (at most 128 per lane) for two
-// work-groups per CU; d = 128 runs one.
+// d <= 64 needs few enough registers (at most 128 per lane) for two
+// work-groups per CU; larger d runs one.
 template <int D>
 constexpr int fwd_blocks_per_cu() {
   return D <= 64 ? 2 : 1;
@@ -272,12 +274,13 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   constexpr bool BAND = MASK != kMaskNone;
   constexpr int KB = key_blocks<D>();
   constexpr int kBlockN = 32 * KB;  // keys per tile
+  constexpr int P = lds_pitch<D>();
   // Two sets of (K tile, V tile), declared as separate objects so the compiler
   // can see that reading one set never depends on the copy filling the other.
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kBlockN * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kBlockN * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kBlockN * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kBlockN * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kBlockN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kBlockN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kBlockN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kBlockN * P];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   st.l = 0.f;
   st.mc = 0.f;
   // the first matrix phase multiplies P = 0 by the V buffer of set 0: zero it
-  for (int i = tid; i < kBlockN * D / 8; i += kThreads) ((FA_LDS u32x4*)(FA_LDS bf16_t*)v_lds0)[i] = u32x4{};
+  for (int i = tid; i < kBlockN * P / 8; i += kThreads) ((FA_LDS u32x4*)(FA_LDS bf16_t*)v_lds0)[i] = u32x4{};
 
   wait_vmem();
   __syncthreads();
@@ -384,15 +387,19 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   }
 }
 
-#define FA_FWD_INSTANCES(E)                                        \
-  template __global__ void fwd_kernel<E, 64, kMaskNone>(FwdParams);   \
-  template __global__ void fwd_kernel<E, 64, kMaskUpper>(FwdParams);  \
-  template __global__ void fwd_kernel<E, 64, kMaskBand>(FwdParams);   \
-  template __global__ void fwd_kernel<E, 128, kMaskNone>(FwdParams);  \
-  template __global__ void fwd_kernel<E, 128, kMaskUpper>(FwdParams); \
-  template __global__ void fwd_kernel<E, 128, kMaskBand>(FwdParams);
-FA_FWD_INSTANCES(Bf16)
-FA_FWD_INSTANCES(F16)
+#define FA_FWD_INSTANCES(E, D)                                    \
+  template __global__ void fwd_kernel<E, D, kMaskNone>(FwdParams);  \
+  template __global__ void fwd_kernel<E, D, kMaskUpper>(FwdParams); \
+  template __global__ void fwd_kernel<E, D, kMaskBand>(FwdParams);
+#define FA_FWD_INSTANCES_D(E) \
+  FA_FWD_INSTANCES(E, 32)     \
+  FA_FWD_INSTANCES(E, 64)     \
+  FA_FWD_INSTANCES(E, 96)     \
+  FA_FWD_INSTANCES(E, 128)    \
+  FA_FWD_INSTANCES(E, 256)
+FA_FWD_INSTANCES_D(Bf16)
+FA_FWD_INSTANCES_D(F16)
+#undef FA_FWD_INSTANCES_D
 #undef FA_FWD_INSTANCES
 
 template <typename E, int D, int MASK>
@@ -438,7 +445,13 @@ hipError_t launch_m(const FwdArgs& a) {
 
 template <typename E>
 hipError_t launch_d(const FwdArgs& a) {
-  return a.g.d == 64 ? launch_m<E, 64>(a) : launch_m<E, 128>(a);
+  switch (a.g.d) {
+    case 32: return launch_m<E, 32>(a);
+    case 64: return launch_m<E, 64>(a);
+    case 96: return launch_m<E, 96>(a);
+    case 128: return launch_m<E, 128>(a);
+    default: return launch_m<E, 256>(a);
+  }
 }
 
 }  // namespace

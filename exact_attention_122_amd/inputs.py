@@ -54,6 +54,13 @@ WORKLOADS = {
     "bnhd_n8192_d128": dict(B=1, H=32, N=8192, d=128, dtype="bf16",
                             causal=False, backward=True, layout="bnhd",
                             seed=1229),
+    #   other head dimensions at the 8k length (H * d = 4096 where it divides)
+    "d32_n8192": dict(B=1, H=128, N=8192, d=32, dtype="bf16", causal=False,
+                      backward=True, seed=1230),
+    "d96_n8192": dict(B=1, H=32, N=8192, d=96, dtype="bf16", causal=False,
+                      backward=True, seed=1231),
+    "d256_n8192": dict(B=1, H=16, N=8192, d=256, dtype="bf16", causal=False,
+                       backward=True, seed=1232),
 }
 
 

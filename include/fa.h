@@ -86,7 +86,7 @@ const char* fa_last_error_detail(void);
  *  O        out  [B, H, N, d] of `dtype` (rounded to nearest even from fp32)
  *  LSE      out  [B, H, N] float32
  *  scale    any finite float (1/sqrt(d) in the usual use)
- *  d        64 or 128
+ *  d        32, 64, 96, 128 or 256 (fp32: at most 128)
  *  dtype    FA_BF16, FA_FP16 or FA_FP32
  * O and LSE must not overlap any input.
  */
@@ -116,7 +116,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  *  dQ, dK, dV      out  [B, H, N, d] of `dtype`
  *  workspace       device scratch of at least fa_bwd_workspace_bytes() bytes,
  *                  16-byte aligned, owned by the caller
- *  d               64 or 128;  dtype FA_BF16 or FA_FP16 (FA_FP32 -> UNSUPPORTED)
+ *  d               32, 64, 96, 128 or 256;  dtype FA_BF16 or FA_FP16
+ *                  (FA_FP32 -> UNSUPPORTED)
  * Outputs and the workspace must not overlap any input or each other.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O,

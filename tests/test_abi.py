@@ -64,8 +64,9 @@ def bwd(*, ptrs=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, dtype=fa.FA_
     (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
     (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
     (dict(d=0), fa.FA_ERR_INVALID_ARGUMENT, "positive"),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "not built"),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=256, dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "fp32"),
     (dict(dtype=7), fa.FA_ERR_INVALID_ARGUMENT, "dtype"),
     (dict(causal=2), fa.FA_ERR_INVALID_ARGUMENT, "causal"),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
@@ -88,7 +89,7 @@ def test_fwd_empty_problem_is_a_no_op(kw):
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16 only"),
-    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=16), fa.FA_ERR_UNSUPPORTED, "not built"),
     (dict(ws=0), fa.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
     (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARGUMENT, "smaller"),
     (dict(ptrs=[P[0]] + P[1:6] + [P[1]] + P[7:9]), fa.FA_ERR_INVALID_ARGUMENT, "dQ overlaps K"),
@@ -110,7 +111,8 @@ def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 64 * 8
     assert fa.fa_bwd_workspace_bytes(1, 3, 65, 64) == 3 * 128 * 8
     assert fa.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 80) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 96) == 64 * 8
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP32) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64, fa.FA_FP16) == 64 * 8
     # general shapes: statistics are per query row
@@ -166,7 +168,7 @@ def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, scale=0.1
     (dict(Nq=-1), fa.FA_ERR_INVALID_ARGUMENT, "negative"),
     (dict(wl=-2), fa.FA_ERR_INVALID_ARGUMENT, "window"),
     (dict(wr=-7), fa.FA_ERR_INVALID_ARGUMENT, "window"),
-    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED, "not built"),
     (dict(qs=_ll(2 * 128 * 64, 128 * 64, 60)), fa.FA_ERR_UNSUPPORTED, "below d"),
     (dict(ks=_ll(2 * 256 * 64, 256 * 64, 68)), fa.FA_ERR_UNSUPPORTED, "multiples of 8"),
     (dict(vs=_ll(-1, 256 * 64, 64)), fa.FA_ERR_UNSUPPORTED, "negative"),

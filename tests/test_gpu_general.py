@@ -244,3 +244,37 @@ def test_legacy_entry_points_equal_the_general_ones_bitwise():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+# ------------------------------------------------------- more head dims ---
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [None, (-1, 0), (40, 0)])
+@pytest.mark.parametrize("d", [32, 96, 256])
+@pytest.mark.parametrize("nq,nk", [(1, 1), (100, 100), (257, 257), (70, 300)])
+def test_head_dims_fwd_bwd(nq, nk, d, window, dtype):
+    g = inputs.generate(1, 2, nq, d, dtype, seed=7500 + d + nq + nk, with_grad_output=True, nk=nk)
+    scale = inputs.default_scale(d)
+    out = _run(g, window, scale, True, dtype)
+    _check(g, out, window, scale, dtype, True)
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_head_dims_fp32_forward(d):
+    for nq, nk, window in ((100, 100, None), (64, 200, (-1, 0)), (150, 150, (20, 0))):
+        g = inputs.generate(1, 2, nq, d, "fp32", seed=7600 + d + nq, nk=nk)
+        scale = inputs.default_scale(d)
+        out = _run(g, window, scale, False, "fp32")
+        _check(g, out, window, scale, "fp32", False)
+
+
+def test_head_dim_96_strided_rows():
+    """d = 96 rows in [B, N, H, d] memory: 192-byte rows, padded only in LDS."""
+    B, H, n, d = 1, 3, 300, 96
+    g = inputs.generate(B, H, n, d, "bf16", seed=7700, with_grad_output=True)
+    q, k, v, do = (to_dev(g[x]).transpose(1, 2).contiguous().transpose(1, 2) for x in ("q", "k", "v", "do"))
+    scale = inputs.default_scale(d)
+    o, lse = fa.fa_fwd_ex(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _check(g, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, (-1, 0), scale, "bf16", True)

@@ -200,7 +200,7 @@ def test_empty_problem_on_gpu():
 
 
 def test_unsupported_requests_raise():
-    q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 1, 64, 80, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="UNSUPPORTED"):
         fa.fa_fwd(q, q, q)
     q = torch.zeros(1, 1, 64, 64, dtype=torch.float64, device="cuda")

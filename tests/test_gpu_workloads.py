@@ -196,3 +196,9 @@ def test_bnhd_n8192_equals_contiguous_bitwise():
                                  rows=rows)
     compare("O", f64(o)[0, 9, rows], ro, TOL["bf16"]["o"], REL_FRO)
     compare("LSE", f64(lse)[0, 9, rows], rl, TOL["bf16"]["lse"])
+
+
+@pytest.mark.parametrize("name,heads_fwd,heads_bwd", [("d32_n8192", [0, 127], [64]), ("d96_n8192", [0, 31], [3]),
+                                                      ("d256_n8192", [0, 15], [9])])
+def test_head_dims_n8192_sampled(name, heads_fwd, heads_bwd):
+    _check_suite(name, heads_fwd=heads_fwd, heads_bwd=heads_bwd)
