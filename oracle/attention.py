@@ -7,12 +7,18 @@ no code with the HIP kernels or their C-ABI library.
 What it computes, one head at a time, in float64, with nothing fused, blocked
 or reordered beyond what the definition states:
 
-  S = scale * Q K^T                 'FlashAttention' (josueisai.com), section on
+  S = scale * Q K^T [+ bias]        'FlashAttention' (josueisai.com), section on
                                     the matrix that should never be stored: the
                                     three-step definition S = QK^T, row softmax,
                                     O = PV. The scale factor is an argument
                                     (the pages omit it; every workload passes
-                                    1/sqrt(d) rounded to float32).
+                                    1/sqrt(d) rounded to float32). An
+                                    optional additive bias [Nq, Nk] (any
+                                    broadcastable shape; -inf removes a key)
+                                    is added to the scaled scores: the masks
+                                    and biases that the page's section on what
+                                    you gain and what not warns may push
+                                    libraries off their fast path.
   masks: S_ij = -inf outside a band key j is visible to query i when
                                     diag_i - left <= j <= diag_i + right,
                                     diag_i = i + Nk - Nq (query rows aligned
@@ -75,8 +81,10 @@ def _band(causal: bool, window):
 
 
 def _scores(q_rows: np.ndarray, row_idx: np.ndarray, k: np.ndarray,
-            scale: float, nq: int, left, right) -> np.ndarray:
+            scale: float, nq: int, left, right, bias_rows=None) -> np.ndarray:
     s = float(scale) * (q_rows @ k.T)
+    if bias_rows is not None:
+        s = s + bias_rows
     if left is None and right is None:
         return s
     diag = row_idx + (k.shape[0] - nq)      # key aligned with each query row
@@ -101,15 +109,21 @@ def _softmax_rows(s: np.ndarray):
     return p, m, l, dead
 
 
-def forward_head(q, k, v, scale: float, causal: bool = False, rows=None, window=None):
+def _bias_2d(bias, nq, nk):
+    return None if bias is None else np.broadcast_to(_as_f64(bias), (nq, nk))
+
+
+def forward_head(q, k, v, scale: float, causal: bool = False, rows=None, window=None, bias=None):
     """One head. q [Nq, d], k [Nk, d], v [Nk, dv] -> O [R, dv], LSE [R].
 
     ``rows`` selects query rows (default: all); masks use the absolute query
     index. ``window`` = (left, right) bounds the visible keys around each
     row's aligned key (None = unbounded); ``causal`` sets right = 0.
+    ``bias`` (broadcastable to [Nq, Nk]) is added to the scaled scores.
     """
     left, right = _band(causal, window)
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    bias = _bias_2d(bias, q.shape[0], k.shape[0])
     if rows is None:
         rows = np.arange(q.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
@@ -117,7 +131,7 @@ def forward_head(q, k, v, scale: float, causal: bool = False, rows=None, window=
     lse = np.zeros(rows.size, dtype=np.float64)
     for c0 in range(0, rows.size, _ROW_CHUNK):
         idx = rows[c0:c0 + _ROW_CHUNK]
-        s = _scores(q[idx], idx, k, scale, q.shape[0], left, right)
+        s = _scores(q[idx], idx, k, scale, q.shape[0], left, right, None if bias is None else bias[idx])
         p, m, l, dead = _softmax_rows(s)
         o[c0:c0 + idx.size] = p @ v
         with np.errstate(divide="ignore"):
@@ -125,17 +139,19 @@ def forward_head(q, k, v, scale: float, causal: bool = False, rows=None, window=
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool = False, window=None):
-    """One head: gradients of sum(O * dO) w.r.t. Q, K, V (LSE not differentiated)."""
+def backward_head(q, k, v, do, scale: float, causal: bool = False, window=None, bias=None):
+    """One head: gradients of sum(O * dO) w.r.t. Q, K, V (LSE and the bias are
+    not differentiated)."""
     left, right = _band(causal, window)
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    bias = _bias_2d(bias, q.shape[0], k.shape[0])
     nq = q.shape[0]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for c0 in range(0, nq, _ROW_CHUNK):
         idx = np.arange(c0, min(nq, c0 + _ROW_CHUNK))
-        s = _scores(q[idx], idx, k, scale, nq, left, right)
+        s = _scores(q[idx], idx, k, scale, nq, left, right, None if bias is None else bias[idx])
         p, _, _, _ = _softmax_rows(s)
         g = do[idx]
         dv += p.T @ g
@@ -169,16 +185,27 @@ def _limit_blas(n_workers):
         return None
 
 
-def forward(q, k, v, scale: float, causal: bool = False, workers=None, window=None):
-    """[..., N, d] batched forward; heads are independent and run in threads."""
+def _bias_heads(bias, lead, nq, nk):
+    """Per-head [Nq, Nk] bias views (None when there is no bias)."""
+    if bias is None:
+        return None
+    b = np.broadcast_to(_as_f64(bias), tuple(lead) + (nq, nk))
+    return b.reshape(-1, nq, nk)
+
+
+def forward(q, k, v, scale: float, causal: bool = False, workers=None, window=None, bias=None):
+    """[..., N, d] batched forward; heads are independent and run in threads.
+    ``bias`` broadcasts to [..., Nq, Nk]."""
     qh, lead = _heads(q)
     kh, _ = _heads(k)
     vh, _ = _heads(v)
+    bh = _bias_heads(bias, lead, qh.shape[1], kh.shape[1])
     n = _pool(workers)
     lim = _limit_blas(n)
     try:
         with ThreadPoolExecutor(n) as ex:
-            res = list(ex.map(lambda i: forward_head(qh[i], kh[i], vh[i], scale, causal, window=window),
+            res = list(ex.map(lambda i: forward_head(qh[i], kh[i], vh[i], scale, causal, window=window,
+                                                           bias=None if bh is None else bh[i]),
                               range(qh.shape[0])))
     finally:
         if lim is not None:
@@ -188,17 +215,19 @@ def forward(q, k, v, scale: float, causal: bool = False, workers=None, window=No
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool = False, workers=None, window=None):
+def backward(q, k, v, do, scale: float, causal: bool = False, workers=None, window=None, bias=None):
     """[..., N, d] batched backward; returns dQ, dK, dV."""
     qh, lead = _heads(q)
     kh, _ = _heads(k)
     vh, _ = _heads(v)
+    bh = _bias_heads(bias, lead, qh.shape[1], kh.shape[1])
     gh, _ = _heads(do)
     n = _pool(workers)
     lim = _limit_blas(n)
     try:
         with ThreadPoolExecutor(n) as ex:
-            res = list(ex.map(lambda i: backward_head(qh[i], kh[i], vh[i], gh[i], scale, causal, window=window),
+            res = list(ex.map(lambda i: backward_head(qh[i], kh[i], vh[i], gh[i], scale, causal, window=window,
+                                                            bias=None if bh is None else bh[i]),
                               range(qh.shape[0])))
     finally:
         if lim is not None:

@@ -24,6 +24,8 @@ MUTATIONS = [
     ("_scores", "row_idx + (k.shape[0] - nq)", "row_idx"),
     ("_scores", "row_idx + (k.shape[0] - nq)", "row_idx + (nq - k.shape[0])"),
     ("_band", "        right = 0\n", "        right = None\n"),
+    ("_scores", "s = s + bias_rows", "s = s - bias_rows"),
+    ("_scores", "s = s + bias_rows", "s = s + float(scale) * bias_rows"),
     ("_softmax_rows", "m = s.max(axis=1)", "m = s.min(axis=1)"),
     ("_softmax_rows", "p = e / np.where(dead, 1.0, l)[:, None]", "p = e / np.where(dead, 1.0, l.max())"),
     ("forward_head", "m + np.log(l)", "np.log(l)"),

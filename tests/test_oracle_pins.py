@@ -55,6 +55,10 @@ def _load_cases():
         return json.load(f)["cases"]
 
 
+def _bias(case):
+    return None if "bias" not in case else _arr(case["bias"])
+
+
 def _window(case):
     w = case.get("window")
     return None if w is None else tuple(w)
@@ -69,7 +73,8 @@ def _rand(shape, seed):
 @pytest.mark.parametrize("case", _load_cases(), ids=lambda c: c["name"])
 def test_hand_worked_forward(case):
     q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
-    o, lse = oracle.forward_head(q, k, v, _eval(case["scale"]), case["causal"], window=_window(case))
+    o, lse = oracle.forward_head(q, k, v, _eval(case["scale"]), case["causal"], window=_window(case),
+                                 bias=_bias(case))
     np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=1e-13)
 
@@ -78,7 +83,7 @@ def test_hand_worked_forward(case):
 def test_hand_worked_backward(case):
     q, k, v, do = (_arr(case[n]) for n in ("q", "k", "v", "do"))
     dq, dk, dv = oracle.backward_head(q, k, v, do, _eval(case["scale"]), case["causal"],
-                                      window=_window(case))
+                                      window=_window(case), bias=_bias(case))
     np.testing.assert_allclose(dq, _arr(case["dq"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(dk, _arr(case["dk"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(dv, _arr(case["dv"]), rtol=0, atol=1e-13)
@@ -338,6 +343,72 @@ def test_band_arguments_are_checked():
         oracle.forward_head(q, q, q, 1.0, causal=True, window=(2, 1))
     with pytest.raises(ValueError):
         oracle.forward_head(q, q, q, 1.0, window=(-1, 0))
+
+
+# ------------------------------------------------------------ additive bias ---
+
+def test_row_constant_bias_moves_lse_only():
+    q, k, v = _rand((9, 4), 90), _rand((13, 4), 91), _rand((13, 3), 92)
+    c = _rand((9, 1), 93)
+    o0, l0 = oracle.forward_head(q, k, v, 0.7, window=(3, 2))
+    o1, l1 = oracle.forward_head(q, k, v, 0.7, window=(3, 2), bias=c)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l0 + c[:, 0], rtol=0, atol=1e-13)
+
+
+def test_log_multiplicity_bias_equals_repeated_keys():
+    # a bias of ln(m_j) on key j weighs it like m_j copies of that key
+    q, k, v = _rand((6, 5), 94), _rand((4, 5), 95), _rand((4, 2), 96)
+    m = np.array([1, 3, 2, 5])
+    o, lse = oracle.forward_head(q, k, v, 0.6, bias=np.log(m)[None, :])
+    o_rep, lse_rep = oracle.forward_head(q, np.repeat(k, m, axis=0), np.repeat(v, m, axis=0), 0.6)
+    np.testing.assert_allclose(o, o_rep, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_rep, rtol=0, atol=1e-13)
+
+
+def test_minus_inf_bias_removes_keys():
+    q, k, v = _rand((5, 4), 97), _rand((8, 4), 98), _rand((8, 3), 99)
+    keep = np.array([1, 0, 1, 1, 0, 0, 1, 1], bool)
+    bias = np.where(keep, 0.0, -np.inf)[None, :]
+    o, lse = oracle.forward_head(q, k, v, 0.9, bias=bias)
+    o_ref, lse_ref = oracle.forward_head(q, k[keep], v[keep], 0.9)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-13)
+    do = _rand((5, 3), 100)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, 0.9, bias=bias)
+    rq, rk, rv = oracle.backward_head(q, k[keep], v[keep], do, 0.9)
+    np.testing.assert_allclose(dq, rq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk[keep], rk, rtol=0, atol=1e-12)
+    assert np.all(dk[~keep] == 0) and np.all(dv[~keep] == 0)
+
+
+def test_bias_matches_torch_sdpa_float_mask_and_autograd():
+    torch = pytest.importorskip("torch")
+    q, k, v = _rand((7, 4), 101), _rand((11, 4), 102), _rand((11, 3), 103)
+    bias, do = _rand((7, 11), 104), _rand((7, 3), 105)
+    o, lse = oracle.forward_head(q, k, v, 0.5, bias=bias)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, 0.5, bias=bias)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    tb = torch.from_numpy(bias)
+    to = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=tb[None],
+                                                          scale=0.5)[0]
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(0.5 * tq @ tk.T + tb, dim=1).detach().numpy(),
+                               rtol=0, atol=1e-13)
+    (to * torch.from_numpy(do)).sum().backward()
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_bias_broadcasts_over_heads_in_the_batched_oracle():
+    q, k, v = _rand((2, 3, 5, 4), 106), _rand((2, 3, 6, 4), 107), _rand((2, 3, 6, 2), 108)
+    bias = _rand((1, 3, 1, 6), 109)           # per head, per key: a key-padding style bias
+    o, lse = oracle.forward(q, k, v, 0.4, bias=bias, workers=1)
+    for b in range(2):
+        for h in range(3):
+            ro, rl = oracle.forward_head(q[b, h], k[b, h], v[b, h], 0.4, bias=bias[0, h])
+            np.testing.assert_allclose(o[b, h], ro, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lse[b, h], rl, rtol=0, atol=1e-14)
 
 
 # -------------------------------------------- blockwise replay (the pages) ---
