@@ -12,7 +12,7 @@ causal masking), backward 2.5x that. Prints ONE JSON line.
 
 `--suite` instead times the general-shape workloads (a sliding window, new
 queries over a long key cache, fp16, a [B, N, H, d] layout, head dimensions
-32, 96 and 256) through
+32, 96 and 256, an additive per-head bias) through
 fa_fwd_ex / fa_bwd_ex and prints one JSON line per workload; there FLOPs are
 4*d per visible (query, key) pair, counted exactly for the mask.
 """
@@ -99,7 +99,7 @@ def visible_pairs(nq, nk, window):
 
 
 SUITE = ("window_n16384_d128_w1024", "prefill_q512_k16384_d128", "fp16_n8192_d128", "bnhd_n8192_d128",
-         "d32_n8192", "d96_n8192", "d256_n8192")
+         "d32_n8192", "d96_n8192", "d256_n8192", "bias_n4096_d128")
 
 
 def run_suite(args):
@@ -129,13 +129,16 @@ def run_suite(args):
                          dtype=torch.uint8, device=dev)
         wl = -1 if window[0] is None else window[0]
         wr = -1 if window[1] is None else window[1]
+        bias = None
+        if "bias" in w:
+            bias = torch.from_numpy(inputs.generate_bias(w["bias"], w["seed"] + 1)).to(dev)
 
         def fwd():
-            fa.fa_fwd_ex(q, k, v, window=(wl, wr), scale=scale, out=o, lse=lse)
+            fa.fa_fwd_ex(q, k, v, window=(wl, wr), scale=scale, out=o, lse=lse, bias=bias)
 
         def bwd():
             fa.fa_bwd_ex(q, k, v, o, do, lse, window=(wl, wr), scale=scale, dq=grads[0], dk=grads[1],
-                         dv=grads[2], workspace=ws)
+                         dv=grads[2], workspace=ws, bias=bias)
 
         res = {}
         pairs = visible_pairs(N, nk, window) * B * H
@@ -153,9 +156,14 @@ def run_suite(args):
             med = ms[len(ms) // 2]
             res[tag] = {"ms": round(med, 4), "tflops": round(flops / med / 1e9, 2),
                         "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        extra = {}
+        if bias is not None:
+            # the bias is read once per (batch, head) in the forward, twice in the backward
+            bias_bytes = B * H * N * nk * 4
+            extra = {"bias_shape": list(w["bias"]), "bias_read_GBps_fwd": round(bias_bytes / res["fwd"]["ms"] / 1e6, 1)}
         print(json.dumps({"suite": name, "dtype": w["dtype"], "layout": layout,
                           "config": {"B": B, "H": H, "Nq": N, "Nk": nk, "d": d,
-                                     "window": [wl, wr], "seed": w["seed"]},
+                                     "window": [wl, wr], "seed": w["seed"]}, **extra,
                           "visible_pairs": pairs, "flops_fwd": 4.0 * d * pairs, **res,
                           "peak": PEAK_BF16_TFLOPS}), flush=True)
 

@@ -96,6 +96,11 @@ int describe(Tensor* t, const long long* strides, const Problem& pr, bool output
   } else {
     t->st = fa::Strides{(long long)pr.H * t->rows * pr.d, (long long)t->rows * pr.d, (long long)pr.d};
   }
+  // the stride of a dimension of size 1 is never used: normalise it (to 0,
+  // or to d for rows, which keeps rows past the end outside the buffer)
+  if (pr.B == 1) t->st.b = 0;
+  if (pr.H == 1) t->st.h = 0;
+  if (t->rows == 1) t->st.r = pr.d;
   const fa::Strides& s = t->st;
   const long long count = pr.bh * t->rows;
   t->ext = Extent{};
@@ -139,6 +144,34 @@ int describe(Tensor* t, const long long* strides, const Problem& pr, bool output
   return FA_OK;
 }
 
+// The optional fp32 bias [B, H, Nq, Nk] (keys contiguous): strides >= 0 (0
+// broadcasts), rows 16-byte aligned. Fills *st and *ext; a null bias is none.
+int describe_bias(const float* bias, const long long* strides, const Problem& pr, fa::Strides* st, Extent* ext) {
+  *ext = Extent{};
+  const long long nk = pr.nk;
+  *st = strides ? fa::Strides{strides[0], strides[1], strides[2]}
+                : fa::Strides{(long long)pr.H * pr.nq * nk, (long long)pr.nq * nk, nk};
+  // strides of dimensions of size 1 are never used
+  if (pr.B == 1) st->b = 0;
+  if (pr.H == 1) st->h = 0;
+  if (pr.nq == 1) st->r = 0;
+  if (!bias || pr.bh * pr.nq * nk == 0) return FA_OK;
+  if (!aligned16(bias)) return fail(FA_ERR_INVALID_ARGUMENT, "bias is not 16-byte aligned");
+  if (st->b < 0 || st->h < 0 || st->r < 0)
+    return fail(FA_ERR_UNSUPPORTED, "bias has a negative stride (%lld, %lld, %lld)", st->b, st->h, st->r);
+  if (st->b % 4 || st->h % 4 || st->r % 4)
+    return fail(FA_ERR_UNSUPPORTED, "bias strides (%lld, %lld, %lld) are not multiples of 4 floats (16 bytes)", st->b,
+                st->h, st->r);
+  if (st->b > LLONG_MAX / 8 / std::max(pr.B, 1) || st->h > LLONG_MAX / 8 / std::max(pr.H, 1) ||
+      st->r > LLONG_MAX / 8 / std::max(pr.nq, 1))
+    return fail(FA_ERR_INVALID_ARGUMENT, "bias strides overflow");
+  const long long span =
+      ((long long)(pr.B - 1) * st->b + (long long)(pr.H - 1) * st->h + (long long)(pr.nq - 1) * st->r + nk) * 4;
+  ext->lo = reinterpret_cast<uintptr_t>(bias);
+  ext->hi = ext->lo + (uintptr_t)span;
+  return FA_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FA_OK;
   return fail(FA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
@@ -147,7 +180,8 @@ int hip_status(hipError_t e, const char* what) {
 // Shared body of fa_fwd and fa_fwd_ex.
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, const Problem& pr,
             const long long* q_strides, const long long* k_strides, const long long* v_strides,
-            const long long* o_strides, float scale, int wl, int wr, void* stream) {
+            const long long* o_strides, const float* bias, const long long* bias_strides, float scale, int wl, int wr,
+            void* stream) {
   int st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if ((st = check_window(wl, wr)) != FA_OK) return st;
@@ -158,8 +192,13 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, co
     return st;
   if (!LSE) return fail(FA_ERR_INVALID_ARGUMENT, "LSE is NULL");
   if (!aligned16(LSE)) return fail(FA_ERR_INVALID_ARGUMENT, "LSE is not 16-byte aligned");
+  fa::Strides sbias;
+  Extent bext;
+  if ((st = describe_bias(bias, bias_strides, pr, &sbias, &bext)) != FA_OK) return st;
+  if (bias && pr.dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "a bias is built for bf16 and fp16 only");
   const Extent lse{reinterpret_cast<uintptr_t>(LSE), reinterpret_cast<uintptr_t>(LSE) + (uintptr_t)(pr.bh * pr.nq * 4)};
-  for (const Tensor* in : {&q, &k, &v}) {
+  Tensor bt{bias, "bias", pr.nq, sbias, bext};
+  for (const Tensor* in : {&q, &k, &v, &bt}) {
     if (overlap(o.ext, in->ext)) return fail(FA_ERR_INVALID_ARGUMENT, "O overlaps %s", in->name);
     if (overlap(lse, in->ext)) return fail(FA_ERR_INVALID_ARGUMENT, "LSE overlaps %s", in->name);
   }
@@ -167,7 +206,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, co
 
   fa::FwdArgs a;
   a.q = Q, a.k = K, a.v = V, a.o = O, a.lse = LSE;
-  a.sq = q.st, a.sk = k.st, a.sv = v.st, a.so = o.st;
+  a.bias = (bias && pr.nk > 0) ? bias : nullptr;
+  a.sq = q.st, a.sk = k.st, a.sv = v.st, a.so = o.st, a.sbias = sbias;
   const int wmax = pr.nq + pr.nk;
   a.g = fa::Geometry{pr.B, pr.H, pr.nq, pr.nk, pr.d, std::min(wl, wmax), std::min(wr, wmax)};
   a.scale = scale;
@@ -184,8 +224,9 @@ size_t workspace_bytes(const Problem& pr) {
 
 // Shared body of fa_bwd and fa_bwd_ex.
 int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
-             void* dK, void* dV, const Problem& pr, const long long* const strides[8], float scale, int wl, int wr,
-             void* workspace, size_t workspace_bytes_given, void* stream) {
+             void* dK, void* dV, const Problem& pr, const long long* const strides[8], const float* bias,
+             const long long* bias_strides, float scale, int wl, int wr, void* workspace,
+             size_t workspace_bytes_given, void* stream) {
   int st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if ((st = check_window(wl, wr)) != FA_OK) return st;
@@ -212,12 +253,16 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   if (workspace_bytes_given < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes_given,
                 need);
+  fa::Strides sbias;
+  Extent bext;
+  if ((st = describe_bias(bias, bias_strides, pr, &sbias, &bext)) != FA_OK) return st;
   const Extent* out_ext[4] = {&dq.ext, &dk.ext, &dv.ext, &ws};
   const char* out_name[4] = {"dQ", "dK", "dV", "workspace"};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 5; ++j)
       if (overlap(*out_ext[i], ins[j]->ext)) return fail(FA_ERR_INVALID_ARGUMENT, "%s overlaps %s", out_name[i], ins[j]->name);
     if (overlap(*out_ext[i], lse)) return fail(FA_ERR_INVALID_ARGUMENT, "%s overlaps LSE", out_name[i]);
+    if (overlap(*out_ext[i], bext)) return fail(FA_ERR_INVALID_ARGUMENT, "%s overlaps the bias", out_name[i]);
     for (int j = i + 1; j < 4; ++j)
       if (overlap(*out_ext[i], *out_ext[j]))
         return fail(FA_ERR_INVALID_ARGUMENT, "%s overlaps %s", out_name[i], out_name[j]);
@@ -226,6 +271,8 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   fa::BwdArgs a;
   a.q = Q, a.k = K, a.v = V, a.o = O, a.dout = dO, a.lse = LSE;
   a.dq = dQ, a.dk = dK, a.dv = dV;
+  a.bias = (bias && pr.nk > 0 && pr.nq > 0) ? bias : nullptr;
+  a.sbias = sbias;
   a.workspace = (float*)workspace;
   a.sq = q.st, a.sk = k.st, a.sv = v.st, a.so = o.st, a.sdo = g.st;
   a.sdq = dq.st, a.sdk = dk.st, a.sdv = dv.st;
@@ -260,19 +307,21 @@ FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float
   int st = check_dims(B, H, N, N, d, dtype, &pr);
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
-  return forward(Q, K, V, O, LSE, pr, nullptr, nullptr, nullptr, nullptr, scale, -1, causal ? 0 : -1, stream);
+  return forward(Q, K, V, O, LSE, pr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, scale, -1, causal ? 0 : -1,
+                 stream);
 }
 
 FA_EXPORT int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq,
                         int Nk, int d, const long long* q_strides, const long long* k_strides,
-                        const long long* v_strides, const long long* o_strides, float scale, int window_left,
-                        int window_right, int dtype, void* stream) {
+                        const long long* v_strides, const long long* o_strides, const float* bias,
+                        const long long* bias_strides, float scale, int window_left, int window_right, int dtype,
+                        void* stream) {
   g_detail[0] = '\0';
   Problem pr;
   int st = check_dims(B, H, Nq, Nk, d, dtype, &pr);
   if (st != FA_OK) return st;
-  return forward(Q, K, V, O, LSE, pr, q_strides, k_strides, v_strides, o_strides, scale, window_left, window_right,
-                 stream);
+  return forward(Q, K, V, O, LSE, pr, q_strides, k_strides, v_strides, o_strides, bias, bias_strides, scale,
+                 window_left, window_right, stream);
 }
 
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
@@ -296,22 +345,23 @@ FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
   const long long* const none[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, none, scale, -1, causal ? 0 : -1, workspace, workspace_bytes,
-                  stream);
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, none, nullptr, nullptr, scale, -1, causal ? 0 : -1, workspace,
+                  workspace_bytes, stream);
 }
 
 FA_EXPORT int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                         void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk, int d,
                         const long long* q_strides, const long long* k_strides, const long long* v_strides,
                         const long long* o_strides, const long long* do_strides, const long long* dq_strides,
-                        const long long* dk_strides, const long long* dv_strides, float scale, int window_left,
-                        int window_right, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                        const long long* dk_strides, const long long* dv_strides, const float* bias,
+                        const long long* bias_strides, float scale, int window_left, int window_right, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   g_detail[0] = '\0';
   Problem pr;
   int st = check_dims(B, H, Nq, Nk, d, dtype, &pr);
   if (st != FA_OK) return st;
   const long long* const strides[8] = {q_strides, k_strides, v_strides, o_strides,
                                        do_strides, dq_strides, dk_strides, dv_strides};
-  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, strides, scale, window_left, window_right, workspace,
-                  workspace_bytes, stream);
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, strides, bias, bias_strides, scale, window_left, window_right,
+                  workspace, workspace_bytes, stream);
 }

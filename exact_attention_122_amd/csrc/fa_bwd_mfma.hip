@@ -29,7 +29,9 @@
 // forward pass: query i is aligned with key i + nk - nq, a band keeps keys
 // [i + nk - nq - wl, i + nk - nq + wr], each work-group visits only the tiles
 // its band touches, and tiles across a band edge set P = 0 on dead pairs. A
-// query row that saw no key (LSE = -inf) gets P = 0 on every key.
+// query row that saw no key (LSE = -inf) gets P = 0 on every key. An
+// optional fp32 bias enters P's exponent as + log2(e) bias; the bias itself is
+// not differentiated.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -51,9 +53,10 @@ struct BwdParams {
   bf16_t* dq;
   bf16_t* dk;
   bf16_t* dv;
+  const float* bias;
   long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, do_sb, do_sh;  // batch / head strides (elements)
-  long long dq_sb, dq_sh, dk_sb, dk_sh, dv_sb, dv_sh;
-  int q_sr, k_sr, v_sr, do_sr, dq_sr, dk_sr, dv_sr;          // row strides (elements)
+  long long dq_sb, dq_sh, dk_sb, dk_sh, dv_sb, dv_sh, bias_sb, bias_sh;
+  int q_sr, k_sr, v_sr, do_sr, dq_sr, dk_sr, dv_sr, bias_sr;  // row strides (elements)
   int heads;
   int nq, nk;
   int nq_pad;    // nq rounded up to a multiple of 64
@@ -122,11 +125,12 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const bf16_t* o, co
 // (across a band edge) set P = 0 where query row qr is outside this lane's
 // [q_lo, q_hi]. Without one the tile holds no masking code at all: query rows
 // past the end are zero rows with zero statistics and add nothing.
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, const float* st,
                                           const RowRead<D>& rrd, const TrRead<D>& trd, const bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
-                                          float c, int q0, int q_lo, int q_hi, int lane, bool masked) {
+                                          float c, int q0, int q_lo, int q_hi, int lane, bool masked,
+                                          const float* bcol, long long bias_sr, int nq) {
   const int hw = lane >> 5;
   f32x16 s[2], dp[2];
 #pragma unroll
@@ -153,6 +157,11 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
       for (int rr = 0; rr < 4; ++rr) {
         const int i = 4 * g + rr;
         float arg = fmaf(s[qb][i], c, -Lv[rr]);
+        if constexpr (BIAS) {
+          // bias[q][key] down this lane's key column (bcol is null past the last key)
+          const int qr = q0 + r0 + rr;
+          if (bcol && qr < nq) arg = fmaf(kLog2e, bcol[qr * bias_sr], arg);
+        }
         if (MASK != kMaskNone && masked) {
           const int qr = q0 + r0 + rr;
           arg = (qr < q_lo || (MASK == kMaskBand && qr > q_hi)) ? -INFINITY : arg;
@@ -199,12 +208,12 @@ struct DkdvCopy {
 // One query tile for this wave's keys wk0 .. wk0 + 31. With a band, rows with
 // q + diag in [wk0 - wr, wk0 + 31 + wl] see some of the keys and rows with
 // q + diag in [wk0 + 31 - wr, wk0 + wl] see all of them.
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 __device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur, const QTileBufs& nxt,
                                             const DkdvCopy<D>& cp, const RowRead<D>& rrd, const TrRead<D>& trd,
                                             const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                             f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const BwdParams& p,
-                                            int wk0, int q_lo, int q_hi, int lane) {
+                                            int wk0, int q_lo, int q_hi, int lane, const float* bcol) {
   const int q0 = t * kTile;
   if (t + 1 < t_end) cp.issue(nxt, q0 + kTile);
   bool live = wk0 < p.nk, masked = false;
@@ -216,12 +225,14 @@ __device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur
       masked = masked || q0 + kTile - 1 + p.diag > wk0 + p.wl;
     }
   }
-  if (live) dkdv_tile<E, D, MASK>(cur.q, cur.d, cur.st, rrd, trd, kf, vf, dk, dv, p.c, q0, q_lo, q_hi, lane, masked);
+  if (live)
+    dkdv_tile<E, D, MASK, BIAS>(cur.q, cur.d, cur.st, rrd, trd, kf, vf, dk, dv, p.c, q0, q_lo, q_hi, lane, masked, bcol,
+                                p.bias_sr, p.nq);
   wait_vmem();
   __syncthreads();
 }
 
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int P = lds_pitch<D>();
   __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * P];
@@ -246,6 +257,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   const int key = wk0 + col;
   // query rows that see this lane's key: [key - diag - wr, key - diag + wl]
   const int q_lo = key - p.diag - p.wr, q_hi = key - p.diag + p.wl;
+  // this lane's bias column (null past the last key)
+  const float* bcol = nullptr;
+  if (BIAS && key < nk) {
+    const int b = head / p.heads;
+    bcol = p.bias + b * p.bias_sb + (head - b * p.heads) * p.bias_sh + key;
+  }
 
   // query tiles of this work-group's band
   int t_begin = 0, t_end = (nq + kTile - 1) / kTile;
@@ -297,9 +314,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
   for (int t = t_begin; t < t_end; t += 2) {
-    dkdv_step<E, D, MASK>(t, t_end, b0, b1, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane);
+    dkdv_step<E, D, MASK, BIAS>(t, t_end, b0, b1, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol);
     if (t + 1 < t_end)
-      dkdv_step<E, D, MASK>(t + 1, t_end, b1, b0, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane);
+      dkdv_step<E, D, MASK, BIAS>(t + 1, t_end, b1, b0, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol);
   }
 
   // lane holds d = 32 db + col for keys wk0 + 8 g + 4 hw + rr
@@ -325,11 +342,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
 // for keys past the end and, with a band, outside this lane's [k_lo, k_hi].
 // MASK_CODE says whether the tile carries that code at all: the unmasked main
 // loop of a kernel without band has no branch in the middle of its tiles.
-template <typename E, int D, int MASK, bool MASK_CODE>
+template <typename E, int D, int MASK, bool BIAS, bool MASK_CODE>
 __device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, const RowRead<D>& rrd,
                                         const TrRead<D>& trd, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32], float lse2, float drow,
-                                        float c, int key0, int k_lo, int k_hi, int lane, bool masked) {
+                                        float c, int key0, int k_lo, int k_hi, int lane, bool masked,
+                                        const float* brow, int nk) {
   const int hw = lane >> 5;
   f32x16 s[2], dpt[2];
 #pragma unroll
@@ -344,10 +362,28 @@ __device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, cons
   }
   bf16x8 ds[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    // bias of this lane's query row for this key block, four consecutive
+    // keys per load (one block at a time, to bound the registers it takes)
+    f32x4 bv[4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kc = key0 + kb * 32 + 8 * g + 4 * hw;
+        bv[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kc + 3 < nk) {
+          bv[g] = *(const f32x4*)(brow + kc);
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (kc + rr < nk) bv[g][rr] = brow[kc + rr];
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float arg = fmaf(s[kb][i], c, -lse2);
+      if constexpr (BIAS) arg = fmaf(kLog2e, bv[i >> 2][i & 3], arg);
       if (MASK_CODE && masked) {
         const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hw + (i & 3);
         arg = (key > k_hi || (MASK == kMaskBand && key < k_lo)) ? -INFINITY : arg;
@@ -355,19 +391,21 @@ __device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, cons
       const float pv = fast_exp2(arg);
       ds[kb * 2 + (i >> 3)][i & 7] = E::cvt(pv * (dpt[kb][i] - drow));
     }
+    if constexpr (BIAS) __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int t = 0; t < 4; ++t) dq[db] = E::mfma(trd(kt, t, db), ds[t], dq[db]);
 }
 
-template <typename E, int D, int MASK, bool MASK_CODE>
+template <typename E, int D, int MASK, bool BIAS, bool MASK_CODE>
 __device__ __forceinline__ void dq_step(int j, int n_tiles, int key_base, const bf16_t* kt, const bf16_t* vt,
                                         bf16_t* kn, bf16_t* vn, const TileDma<kTile, D, kThreads>& dma,
                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                         const RowRead<D>& rrd, const TrRead<D>& trd, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32], float lse2, float drow,
-                                        const BwdParams& p, int k_lo, int k_hi, int wq0, int lane) {
+                                        const BwdParams& p, int k_lo, int k_hi, int wq0, int lane, const float* brow) {
   const int key0 = key_base + j * kTile;
   if (j + 1 < n_tiles) {
     dma.issue(krs, kn, key0 + kTile, 2u * p.k_sr);
@@ -383,7 +421,9 @@ __device__ __forceinline__ void dq_step(int j, int n_tiles, int key_base, const 
       masked = masked || key0 < wq0 + 31 + p.diag - p.wl;
     }
   }
-  if (live) dq_tile<E, D, MASK, MASK_CODE>(kt, vt, rrd, trd, qf, df, dq, lse2, drow, p.c, key0, k_lo, k_hi, lane, masked);
+  if (live)
+    dq_tile<E, D, MASK, BIAS, MASK_CODE>(kt, vt, rrd, trd, qf, df, dq, lse2, drow, p.c, key0, k_lo, k_hi, lane, masked,
+                                         brow, p.nk);
   wait_vmem();
   __syncthreads();
 }
@@ -395,7 +435,7 @@ constexpr int dq_blocks_per_cu() {
   return D >= 256 ? 1 : 2;
 }
 
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(BwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
   constexpr int P = lds_pitch<D>();
@@ -418,6 +458,12 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   const int q_row0 = qblk * kRowsPerBlock;
   const int wq0 = q_row0 + wave * kRowsPerWave;
   const int qi = wq0 + col;
+  // bias row of this lane's query (rows past nq read the last row; unused)
+  const float* brow = nullptr;
+  if (BIAS) {
+    const int b = head / p.heads;
+    brow = p.bias + b * p.bias_sb + (head - b * p.heads) * p.bias_sh + (long long)min(qi, nq - 1) * p.bias_sr;
+  }
   // live keys of this lane's row: [k_lo, k_hi]
   const int k_lo = BAND ? qi + p.diag - p.wl : 0;
   const int k_hi = BAND ? min(nk - 1, qi + p.diag + p.wr) : nk - 1;
@@ -478,19 +524,19 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   // has the masking code.
   const int n_main = BAND ? n_tiles : min(n_tiles, nk / kTile);
   for (int j = 0; j < n_main; j += 2) {
-    dq_step<E, D, MASK, BAND>(j, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf, df,
-                              dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+    dq_step<E, D, MASK, BIAS, BAND>(j, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf, df,
+                              dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
     if (j + 1 < n_main)
-      dq_step<E, D, MASK, BAND>(j + 1, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+      dq_step<E, D, MASK, BIAS, BAND>(j + 1, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
   }
   if (!BAND && n_main < n_tiles) {
     if (n_main & 1)
-      dq_step<E, D, MASK, true>(n_main, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+      dq_step<E, D, MASK, BIAS, true>(n_main, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
     else
-      dq_step<E, D, MASK, true>(n_main, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane);
+      dq_step<E, D, MASK, BIAS, true>(n_main, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf,
+                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
   }
 
   if (qi < nq) {
@@ -507,13 +553,16 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   }
 }
 
+#define FA_BWD_INSTANCES_B(E, D, B)                                     \
+  template __global__ void dkdv_kernel<E, D, kMaskNone, B>(BwdParams);  \
+  template __global__ void dkdv_kernel<E, D, kMaskUpper, B>(BwdParams); \
+  template __global__ void dkdv_kernel<E, D, kMaskBand, B>(BwdParams);  \
+  template __global__ void dq_kernel<E, D, kMaskNone, B>(BwdParams);    \
+  template __global__ void dq_kernel<E, D, kMaskUpper, B>(BwdParams);   \
+  template __global__ void dq_kernel<E, D, kMaskBand, B>(BwdParams);
 #define FA_BWD_INSTANCES(E, D)                                                                             \
-  template __global__ void dkdv_kernel<E, D, kMaskNone>(BwdParams);                                       \
-  template __global__ void dkdv_kernel<E, D, kMaskUpper>(BwdParams);                                      \
-  template __global__ void dkdv_kernel<E, D, kMaskBand>(BwdParams);                                       \
-  template __global__ void dq_kernel<E, D, kMaskNone>(BwdParams);                                         \
-  template __global__ void dq_kernel<E, D, kMaskUpper>(BwdParams);                                        \
-  template __global__ void dq_kernel<E, D, kMaskBand>(BwdParams);                                         \
+  FA_BWD_INSTANCES_B(E, D, false)                                                                         \
+  FA_BWD_INSTANCES_B(E, D, true)                                                                          \
   template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
                                                   Strides, int, int, int, long long);
 #define FA_BWD_INSTANCES_D(E) \
@@ -526,8 +575,9 @@ FA_BWD_INSTANCES_D(Bf16)
 FA_BWD_INSTANCES_D(F16)
 #undef FA_BWD_INSTANCES_D
 #undef FA_BWD_INSTANCES
+#undef FA_BWD_INSTANCES_B
 
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 hipError_t launch(const BwdArgs& a) {
   const Geometry& g = a.g;
   BwdParams p;
@@ -546,6 +596,8 @@ hipError_t launch(const BwdArgs& a) {
   p.dq_sb = a.sdq.b, p.dq_sh = a.sdq.h, p.dq_sr = (int)a.sdq.r;
   p.dk_sb = a.sdk.b, p.dk_sh = a.sdk.h, p.dk_sr = (int)a.sdk.r;
   p.dv_sb = a.sdv.b, p.dv_sh = a.sdv.h, p.dv_sr = (int)a.sdv.r;
+  p.bias = a.bias;
+  p.bias_sb = a.sbias.b, p.bias_sh = a.sbias.h, p.bias_sr = (int)a.sbias.r;
   p.heads = g.heads;
   p.nq = g.nq;
   p.nk = g.nk;
@@ -572,34 +624,39 @@ hipError_t launch(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (p.nkb > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<E, D, MASK>), dim3((unsigned)(p.nkb * bh)), dim3(kThreads), 0, a.stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<E, D, MASK, BIAS>), dim3((unsigned)(p.nkb * bh)), dim3(kThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.nqb > 0) {
-    hipLaunchKernelGGL((dq_kernel<E, D, MASK>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0, a.stream, p);
+    hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0, a.stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <typename E, int D>
+template <typename E, int D, bool BIAS>
 hipError_t launch_m(const BwdArgs& a) {
   switch (a.g.mask_kind()) {
-    case kMaskNone: return launch<E, D, kMaskNone>(a);
-    case kMaskUpper: return launch<E, D, kMaskUpper>(a);
-    default: return launch<E, D, kMaskBand>(a);
+    case kMaskNone: return launch<E, D, kMaskNone, BIAS>(a);
+    case kMaskUpper: return launch<E, D, kMaskUpper, BIAS>(a);
+    default: return launch<E, D, kMaskBand, BIAS>(a);
   }
+}
+
+template <typename E, int D>
+hipError_t launch_b(const BwdArgs& a) {
+  return a.bias ? launch_m<E, D, true>(a) : launch_m<E, D, false>(a);
 }
 
 template <typename E>
 hipError_t launch_d(const BwdArgs& a) {
   switch (a.g.d) {
-    case 32: return launch_m<E, 32>(a);
-    case 64: return launch_m<E, 64>(a);
-    case 96: return launch_m<E, 96>(a);
-    case 128: return launch_m<E, 128>(a);
-    default: return launch_m<E, 256>(a);
+    case 32: return launch_b<E, 32>(a);
+    case 64: return launch_b<E, 64>(a);
+    case 96: return launch_b<E, 96>(a);
+    case 128: return launch_b<E, 128>(a);
+    default: return launch_b<E, 256>(a);
   }
 }
 

@@ -46,6 +46,10 @@
 //    -inf. A row that sees no key ends with l = 0: O = 0 and LSE = -inf.
 //  * Tensors are addressed through per-tensor batch, head and row strides
 //    (d contiguous), so views of other layouts need no copy.
+//  * An optional fp32 bias is added to the scaled scores. Its kernels work in
+//    log2 units from the start (y = c s + log2(e) bias, one FMA) instead of
+//    raw score units, and each lane loads the bias of its query row, four
+//    consecutive keys per 16-byte load.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -70,8 +74,9 @@ struct FwdParams {
   const bf16_t* v;
   bf16_t* o;
   float* lse;
-  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch / head strides (elements)
-  int q_sr, k_sr, v_sr, o_sr;                                // row strides (elements)
+  const float* bias;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, bias_sb, bias_sh;  // batch / head strides (elements)
+  int q_sr, k_sr, v_sr, o_sr, bias_sr;                                        // row strides (elements)
   int heads;
   int nq, nk;
   int diag;      // nk - nq: the key aligned with query 0
@@ -80,7 +85,7 @@ struct FwdParams {
   int nblocks;   // work-groups in the grid
   float c;       // |scale| * log2(e)
   float scale_abs;
-  float thr;     // lazy-rescale threshold in raw score units
+  float thr;     // lazy-rescale threshold in raw score units (kernels without bias)
   uint32_t qsign;  // 0x80008000 flips two bf16 signs at once when scale < 0
 };
 
@@ -147,18 +152,43 @@ __device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* 
   for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
 }
 
-// Softmax phase for the tile whose scores are in st.s. `masked` tiles (band
-// edges, ragged end) set the scores of dead keys to -inf first.
-template <typename E, int D, int KB, int MASK>
+// Softmax phase for the tile whose scores are in st.s. With a bias the scores
+// become y = c s + log2(e) bias (log2 units) first; `masked` tiles (band
+// edges, ragged end) then set the scores of dead keys to -inf.
+template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
-                                              bool masked) {
+                                              bool masked, const float* brow) {
   constexpr int kN = 16 * KB;  // scores per lane
   const int hw = lane >> 5;
+  // scale of the working units: raw scores without bias, log2 units with one
+  const float cu = BIAS ? 1.f : p.c;
+  const float thr = BIAS ? 8.f : p.thr;
   float x[kN];
 #pragma unroll
   for (int b = 0; b < KB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[16 * b + r] = st.s[b][r];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kc = key0 + 32 * b + 8 * g + 4 * hw;  // keys kc .. kc + 3 of registers 4 g .. 4 g + 3
+        f32x4 bv = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kc + 3 < p.nk) {
+          bv = *(const f32x4*)(brow + kc);
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (kc + rr < p.nk) bv[rr] = brow[kc + rr];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[16 * b + 4 * g + rr] = fmaf(x[16 * b + 4 * g + rr], p.c, kLog2e * bv[rr]);
+        // one key block's loads at a time: the bias must not take 16 KB x 4
+        // of registers beside the scores
+        if (g == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+  }
   if (masked) {
     // live keys of this row: [lo, hi]
     const int hi = MASK != kMaskNone ? min(qi + p.diag + p.wr, p.nk - 1) : p.nk - 1;
@@ -187,10 +217,10 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
   }
   mx = pair_max(mx);
 
-  if (wave_any(!(mx <= st.m + p.thr))) {
+  if (wave_any(!(mx <= st.m + thr))) {
     const float mnew = fmaxf(st.m, mx);
-    const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c;
-    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m * p.c - ms);
+    const float ms = (mnew == -INFINITY) ? 0.f : mnew * cu;
+    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m * cu - ms);
     st.l *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.acc[db] *= alpha;
@@ -203,7 +233,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
   // to back instead of FMA -> exp -> add chains.
   const float nmc = -st.mc;
 #pragma unroll
-  for (int i = 0; i < kN; ++i) x[i] = fmaf(x[i], p.c, nmc);
+  for (int i = 0; i < kN; ++i) x[i] = fmaf(x[i], cu, nmc);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kN; ++i) x[i] = fast_exp2(x[i]);
@@ -235,7 +265,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 // j never depends on the copy into the other set. Every wave runs every tile
 // of its work-group: a tile wholly outside a wave's band has all scores at
 // -inf, so its p are 0 and it changes nothing.
-template <typename E, int D, int KB, int MASK>
+template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, bool group_b, const bf16_t* kt,
                                               const bf16_t* vt,
                                               bf16_t* kn, bf16_t* vn,
@@ -243,7 +273,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const RowRead<D>& krd, const TrRead<D>& vrd,
                                               const bf16x8 (&qf)[D / 16], RowState<D, KB>& st, const FwdParams& p,
-                                              int wq0, int qi, int lane) {
+                                              int wq0, int qi, int lane, const float* brow) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
   if (!group_b) {
@@ -257,7 +287,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
-  softmax_phase<E, D, KB, MASK>(st, p, key0, qi, lane, masked);
+  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow);
   wait_vmem();
   __syncthreads();
 }
@@ -269,7 +299,7 @@ constexpr int fwd_blocks_per_cu() {
   return D <= 64 ? 2 : 1;
 }
 
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(FwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
   constexpr int KB = key_blocks<D>();
@@ -300,6 +330,8 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   const int q_row0 = qblk * kBlockM;
   const int wq0 = q_row0 + wave * 32;
   const int qi = wq0 + col;
+  // bias row of this lane's query (rows past nq read the last row; unused)
+  const float* brow = BIAS ? p.bias + hb * p.bias_sb + hh * p.bias_sh + (long long)min(qi, nq - 1) * p.bias_sr : nullptr;
 
   // K/V tiles of this work-group's band: [key_base, key_base + n_tiles * kBlockN)
   const int q_last = min(nq, q_row0 + kBlockM) - 1;
@@ -357,14 +389,14 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   if (group_b) __syncthreads();
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
-    fwd_iteration<E, D, KB, MASK>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane);
-    fwd_iteration<E, D, KB, MASK>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs,
-                                  krd, vrd, qf, st, p, wq0, qi, lane);
+    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+                                  vrd, qf, st, p, wq0, qi, lane, brow);
+    fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs,
+                                  krd, vrd, qf, st, p, wq0, qi, lane, brow);
   }
   if (j < n_tiles)
-    fwd_iteration<E, D, KB, MASK>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane);
+    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+                                  vrd, qf, st, p, wq0, qi, lane, brow);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
   pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) __syncthreads();
@@ -383,14 +415,20 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
         w.y = pack2<E>(st.acc[db][4 * g + 2] * inv, st.acc[db][4 * g + 3] * inv);
         *(uint2*)(orow + db * 32 + 8 * g + 4 * hw) = w;
       }
-    if (hw == 0) p.lse[(long long)head * nq + qi] = lt > 0.f ? st.m * p.scale_abs + __logf(lt) : -INFINITY;
+    // the reference point m is in raw score units (scale |scale|) or, with a
+    // bias, in log2 units (scale ln 2)
+    const float unit = BIAS ? kLn2 : p.scale_abs;
+    if (hw == 0) p.lse[(long long)head * nq + qi] = lt > 0.f ? st.m * unit + __logf(lt) : -INFINITY;
   }
 }
 
-#define FA_FWD_INSTANCES(E, D)                                    \
-  template __global__ void fwd_kernel<E, D, kMaskNone>(FwdParams);  \
-  template __global__ void fwd_kernel<E, D, kMaskUpper>(FwdParams); \
-  template __global__ void fwd_kernel<E, D, kMaskBand>(FwdParams);
+#define FA_FWD_INSTANCES_B(E, D, B)                                   \
+  template __global__ void fwd_kernel<E, D, kMaskNone, B>(FwdParams);  \
+  template __global__ void fwd_kernel<E, D, kMaskUpper, B>(FwdParams); \
+  template __global__ void fwd_kernel<E, D, kMaskBand, B>(FwdParams);
+#define FA_FWD_INSTANCES(E, D)      \
+  FA_FWD_INSTANCES_B(E, D, false) \
+  FA_FWD_INSTANCES_B(E, D, true)
 #define FA_FWD_INSTANCES_D(E) \
   FA_FWD_INSTANCES(E, 32)     \
   FA_FWD_INSTANCES(E, 64)     \
@@ -401,8 +439,9 @@ FA_FWD_INSTANCES_D(Bf16)
 FA_FWD_INSTANCES_D(F16)
 #undef FA_FWD_INSTANCES_D
 #undef FA_FWD_INSTANCES
+#undef FA_FWD_INSTANCES_B
 
-template <typename E, int D, int MASK>
+template <typename E, int D, int MASK, bool BIAS>
 hipError_t launch(const FwdArgs& a) {
   FwdParams p;
   p.q = (const bf16_t*)a.q;
@@ -414,6 +453,8 @@ hipError_t launch(const FwdArgs& a) {
   p.k_sb = a.sk.b, p.k_sh = a.sk.h, p.k_sr = (int)a.sk.r;
   p.v_sb = a.sv.b, p.v_sh = a.sv.h, p.v_sr = (int)a.sv.r;
   p.o_sb = a.so.b, p.o_sh = a.so.h, p.o_sr = (int)a.so.r;
+  p.bias = a.bias;
+  p.bias_sb = a.sbias.b, p.bias_sh = a.sbias.h, p.bias_sr = (int)a.sbias.r;
   p.heads = a.g.heads;
   p.nq = a.g.nq;
   p.nk = a.g.nk;
@@ -430,27 +471,32 @@ hipError_t launch(const FwdArgs& a) {
   p.c = fmaxf(p.scale_abs * kLog2e, 1e-30f);
   p.thr = p.scale_abs > 0.f ? 8.f / p.c : 3.0e38f;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<E, D, MASK>), dim3(p.nblocks), dim3(kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<E, D, MASK, BIAS>), dim3(p.nblocks), dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
-template <typename E, int D>
+template <typename E, int D, bool BIAS>
 hipError_t launch_m(const FwdArgs& a) {
   switch (a.g.mask_kind()) {
-    case kMaskNone: return launch<E, D, kMaskNone>(a);
-    case kMaskUpper: return launch<E, D, kMaskUpper>(a);
-    default: return launch<E, D, kMaskBand>(a);
+    case kMaskNone: return launch<E, D, kMaskNone, BIAS>(a);
+    case kMaskUpper: return launch<E, D, kMaskUpper, BIAS>(a);
+    default: return launch<E, D, kMaskBand, BIAS>(a);
   }
+}
+
+template <typename E, int D>
+hipError_t launch_b(const FwdArgs& a) {
+  return a.bias ? launch_m<E, D, true>(a) : launch_m<E, D, false>(a);
 }
 
 template <typename E>
 hipError_t launch_d(const FwdArgs& a) {
   switch (a.g.d) {
-    case 32: return launch_m<E, 32>(a);
-    case 64: return launch_m<E, 64>(a);
-    case 96: return launch_m<E, 96>(a);
-    case 128: return launch_m<E, 128>(a);
-    default: return launch_m<E, 256>(a);
+    case 32: return launch_b<E, 32>(a);
+    case 64: return launch_b<E, 64>(a);
+    case 96: return launch_b<E, 96>(a);
+    case 128: return launch_b<E, 128>(a);
+    default: return launch_b<E, 256>(a);
   }
 }
 

@@ -44,7 +44,8 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;  // contiguous [B, H, nq]
-  Strides sq, sk, sv, so;
+  const float* bias;  // additive bias on the scaled scores, or null
+  Strides sq, sk, sv, so, sbias;  // sbias: batch, head, query-row strides; keys contiguous
   Geometry g;
   float scale;  // multiplies Q K^T before the softmax
   int dtype;
@@ -58,11 +59,12 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;  // contiguous [B, H, nq]
+  const float* bias;  // additive bias on the scaled scores, or null
   void* dq;
   void* dk;
   void* dv;
   float* workspace;  // bwd_workspace_bytes(B * H, nq) bytes: per-row statistics
-  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv, sbias;
   Geometry g;
   float scale;
   int dtype;

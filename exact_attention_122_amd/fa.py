@@ -56,12 +56,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     lp = ctypes.POINTER(ctypes.c_longlong)
     lib.fa_fwd_ex.restype = i
-    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, lp, lp, lp, lp, f, i, i, i, vp]
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, lp, lp, lp, lp, vp, lp, f, i, i, i, vp]
     lib.fa_bwd_ex_workspace_bytes.restype = sz
     lib.fa_bwd_ex_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_ex.restype = i
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
-                              lp, lp, lp, lp, lp, lp, lp, lp, f, i, i, i, vp, sz, vp]
+                              lp, lp, lp, lp, lp, lp, lp, lp, vp, lp, f, i, i, i, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -197,6 +197,19 @@ def _strides(t, name):
     return (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
+def _bias_arg(bias, q, B, H, Nq, Nk):
+    """(pointer, strides) of an optional float32 bias broadcastable to [B, H, Nq, Nk]."""
+    import torch
+    if bias is None:
+        return None, None
+    if bias.dtype != torch.float32 or bias.device != q.device:
+        raise RuntimeError("bias must be a float32 tensor on Q's device")
+    b = bias.expand(B, H, Nq, Nk)
+    if Nk > 1 and b.stride(3) != 1:
+        raise RuntimeError("bias: the key dimension must be contiguous")
+    return b.data_ptr(), (ctypes.c_longlong * 3)(b.stride(0), b.stride(1), b.stride(2))
+
+
 def _ex_operands(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise RuntimeError("expected [B, H, rows, d] tensors")
@@ -213,12 +226,14 @@ def _ex_operands(q, k, v):
 
 
 def fa_fwd_ex(q, k, v, causal: bool = False, window=None, scale: float | None = None,
-              out=None, lse=None):
+              out=None, lse=None, bias=None):
     """O, LSE for Nq queries over Nk keys with a band mask and strided views.
 
     ``window`` = (left, right) bounds the visible keys around each query's
     aligned key i + Nk - Nq (None = unbounded); ``causal`` sets right = 0.
-    Any [B, H, rows, d] views with d contiguous are accepted (see include/fa.h).
+    ``bias`` (float32, broadcastable to [B, H, Nq, Nk]) is added to the scaled
+    scores. Any [B, H, rows, d] views with d contiguous are accepted (see
+    include/fa.h).
     """
     import torch
     B, H, Nq, Nk, d = _ex_operands(q, k, v)
@@ -233,9 +248,10 @@ def fa_fwd_ex(q, k, v, causal: bool = False, window=None, scale: float | None = 
         raise RuntimeError("out must be [B, H, Nq, d] of Q's dtype and device")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
         raise RuntimeError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    bp, bs = _bias_arg(bias, q, B, H, Nq, Nk)
     st = load_library().fa_fwd_ex(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
-        _strides(q, "Q"), _strides(k, "K"), _strides(v, "V"), _strides(out, "O"),
+        _strides(q, "Q"), _strides(k, "K"), _strides(v, "V"), _strides(out, "O"), bp, bs,
         float(scale), left, right, _dtype_code(q), _stream(q))
     _check(st, "fa_fwd_ex")
     return out, lse
@@ -246,8 +262,8 @@ def fa_bwd_ex_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: i
 
 
 def fa_bwd_ex(q, k, v, o, do, lse, causal: bool = False, window=None, scale: float | None = None,
-              dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV for O, LSE = fa_fwd_ex(q, k, v, causal, window, scale)."""
+              dq=None, dk=None, dv=None, workspace=None, bias=None):
+    """dQ, dK, dV for O, LSE = fa_fwd_ex(q, k, v, causal, window, scale, bias=bias)."""
     import torch
     B, H, Nq, Nk, d = _ex_operands(q, k, v)
     left, right = _band(causal, window)
@@ -268,11 +284,12 @@ def fa_bwd_ex(q, k, v, o, do, lse, causal: bool = False, window=None, scale: flo
     need = fa_bwd_ex_workspace_bytes(B, H, Nq, Nk, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    bp, bs = _bias_arg(bias, q, B, H, Nq, Nk)
     st = load_library().fa_bwd_ex(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
         _strides(q, "Q"), _strides(k, "K"), _strides(v, "V"), _strides(o, "O"), _strides(do, "dO"),
-        _strides(dq, "dQ"), _strides(dk, "dK"), _strides(dv, "dV"),
+        _strides(dq, "dQ"), _strides(dk, "dK"), _strides(dv, "dV"), bp, bs,
         float(scale), left, right, code, workspace.data_ptr(), workspace.numel(), _stream(q))
     _check(st, "fa_bwd_ex")
     return dq, dk, dv

@@ -61,6 +61,10 @@ WORKLOADS = {
                       backward=True, seed=1231),
     "d256_n8192": dict(B=1, H=16, N=8192, d=256, dtype="bf16", causal=False,
                        backward=True, seed=1232),
+    #   an additive fp32 bias per head, shared over the batch (the shape of a
+    #   learned relative-position bias), drawn N(0,1) after Q, K, V, dO
+    "bias_n4096_d128": dict(B=2, H=16, N=4096, d=128, dtype="bf16", causal=False,
+                            backward=True, bias=(1, 16, 4096, 4096), seed=1233),
 }
 
 
@@ -149,6 +153,11 @@ def generate_workload(name: str) -> dict:
     w = WORKLOADS[name]
     return generate(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"],
                     with_grad_output=w["backward"], nk=w.get("nk"))
+
+
+def generate_bias(shape, seed: int) -> np.ndarray:
+    """A float32 N(0,1) bias of `shape` from its own PCG64(seed)."""
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(size=shape, dtype=np.float32)
 
 
 def default_scale(d: int) -> float:

@@ -141,6 +141,15 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
  *             its own address (FA_ERR_INVALID_ARGUMENT otherwise). Inputs may
  *             share memory (e.g. one packed QKV tensor, or a batch or head
  *             stride of 0 to broadcast K and V).
+ *  bias     NULL, or a float32 additive bias on the scaled scores:
+ *           S = scale * Q K^T + bias, with bias[b, h, i, j] at
+ *           bias + b*s0 + h*s1 + i*s2 + j for bias_strides {s0, s1, s2}
+ *           (NULL = contiguous [B, H, Nq, Nk]); strides >= 0 (0 broadcasts,
+ *           e.g. {0, 0, 0} for one key-padding row shared by all), multiples
+ *           of 4 floats, base 16-byte aligned. Entries must be finite or -inf
+ *           (-inf removes that key for that query: an arbitrary mask). It is
+ *           applied before the band mask and is an input only. 16-bit dtypes
+ *           only (FA_FP32 with a bias -> FA_ERR_UNSUPPORTED).
  *  window_left, window_right  -1 or >= 0 (FA_ERR_INVALID_ARGUMENT otherwise)
  * The address range of O (lowest to highest element) and LSE must not overlap
  * any input's.
@@ -149,6 +158,7 @@ int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
               int B, int H, int Nq, int Nk, int d,
               const long long* q_strides, const long long* k_strides,
               const long long* v_strides, const long long* o_strides,
+              const float* bias, const long long* bias_strides,
               float scale, int window_left, int window_right, int dtype,
               void* stream);
 
@@ -167,9 +177,12 @@ size_t fa_bwd_ex_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype)
  *  Q, O, dO, dQ  [B, H, Nq, d];  K, V, dK, dV  [B, H, Nk, d]
  *  strides       as fa_fwd_ex, one set per tensor; dQ, dK, dV must each give
  *                every element its own address
+ *  bias          the bias fa_fwd_ex was given (or NULL); it is not
+ *                differentiated
  *  dtype         FA_BF16 or FA_FP16 (FA_FP32 -> UNSUPPORTED)
  * The address ranges of dQ, dK, dV and the workspace must not overlap any
- * input's, LSE's or each other's (separate gradient buffers).
+ * input's (the bias included), LSE's or each other's (separate gradient
+ * buffers).
  */
 int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
               const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
@@ -178,6 +191,7 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
               const long long* v_strides, const long long* o_strides,
               const long long* do_strides, const long long* dq_strides,
               const long long* dk_strides, const long long* dv_strides,
+              const float* bias, const long long* bias_strides,
               float scale, int window_left, int window_right, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 

@@ -150,17 +150,18 @@ def _ll(*xs):
 
 
 def fwd_ex(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=128, Nk=256, d=64,
-           qs=None, ks=None, vs=None, os_=None, scale=0.125, wl=-1, wr=-1, dtype=fa.FA_BF16):
+           qs=None, ks=None, vs=None, os_=None, bias=None, bs=None, scale=0.125, wl=-1, wr=-1,
+           dtype=fa.FA_BF16):
     lib = fa.load_library()
-    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, qs, ks, vs, os_, scale, wl, wr, dtype, None)
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, qs, ks, vs, os_, bias, bs, scale, wl, wr, dtype, None)
 
 
-def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, scale=0.125, wl=-1, wr=-1,
-           dtype=fa.FA_BF16, ws=P[9], ws_bytes=1 << 20):
+def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, bias=None, bs=None, scale=0.125, wl=-1,
+           wr=-1, dtype=fa.FA_BF16, ws=P[9], ws_bytes=1 << 20):
     lib = fa.load_library()
     ptrs = ptrs or P[:9]
     strides = strides or [None] * 8
-    return lib.fa_bwd_ex(*ptrs, B, H, Nq, Nk, d, *strides, scale, wl, wr, dtype, ws, ws_bytes, None)
+    return lib.fa_bwd_ex(*ptrs, B, H, Nq, Nk, d, *strides, bias, bs, scale, wl, wr, dtype, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -171,7 +172,7 @@ def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, scale=0.1
     (dict(d=80), fa.FA_ERR_UNSUPPORTED, "not built"),
     (dict(qs=_ll(2 * 128 * 64, 128 * 64, 60)), fa.FA_ERR_UNSUPPORTED, "below d"),
     (dict(ks=_ll(2 * 256 * 64, 256 * 64, 68)), fa.FA_ERR_UNSUPPORTED, "multiples of 8"),
-    (dict(vs=_ll(-1, 256 * 64, 64)), fa.FA_ERR_UNSUPPORTED, "negative"),
+    (dict(vs=_ll(2 * 256 * 64, -64, 64)), fa.FA_ERR_UNSUPPORTED, "negative"),
     (dict(dtype=fa.FA_FP32, qs=_ll(2 * 128 * 64, 128 * 64, 66)), fa.FA_ERR_UNSUPPORTED, "multiples of 4"),
     # O's heads share memory: two elements at one address
     (dict(os_=_ll(128 * 64, 0, 64)), fa.FA_ERR_INVALID_ARGUMENT, "one address"),
@@ -179,6 +180,12 @@ def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, scale=0.1
     (dict(o=P[1]), fa.FA_ERR_INVALID_ARGUMENT, "O overlaps K"),
     (dict(Nk=1 << 20, ks=_ll(0, 0, 1024)), fa.FA_ERR_UNSUPPORTED, "2 GiB"),
     (dict(Nq=(1 << 28) + 1), fa.FA_ERR_UNSUPPORTED, "2^28"),
+    (dict(bias=P[10] + 4), fa.FA_ERR_INVALID_ARGUMENT, "bias is not 16-byte aligned"),
+    (dict(bias=P[10], bs=_ll(0, 0, 6)), fa.FA_ERR_UNSUPPORTED, "multiples of 4 floats"),
+    (dict(bias=P[10], bs=_ll(0, -4, 0)), fa.FA_ERR_UNSUPPORTED, "negative"),
+    (dict(bias=P[10], Nk=255), fa.FA_ERR_UNSUPPORTED, "multiples of 4 floats"),
+    (dict(bias=P[10], dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16 only"),
+    (dict(bias=P[10], o=P[10] + 256), fa.FA_ERR_INVALID_ARGUMENT, "O overlaps bias"),
 ])
 def test_fwd_ex_rejects_on_the_host(kw, status, needle):
     assert fwd_ex(**kw) == status
@@ -206,6 +213,8 @@ def test_fwd_ex_inputs_may_share_memory():
     (dict(ptrs=P[:6] + [P[7]] + P[7:9]), fa.FA_ERR_INVALID_ARGUMENT, "dQ overlaps dK"),
     (dict(strides=[None] * 5 + [_ll(2 * 128 * 64, 0, 64)] + [None] * 2), fa.FA_ERR_INVALID_ARGUMENT, "one address"),
     (dict(strides=[None] * 4 + [_ll(2 * 128 * 64, 128 * 64, 40)] + [None] * 3), fa.FA_ERR_UNSUPPORTED, "below d"),
+    (dict(bias=P[10], ptrs=P[:8] + [P[10] + 64]), fa.FA_ERR_INVALID_ARGUMENT, "dV overlaps the bias"),
+    (dict(bias=P[10], bs=_ll(0, 0, 2)), fa.FA_ERR_UNSUPPORTED, "multiples of 4 floats"),
 ])
 def test_bwd_ex_rejects_on_the_host(kw, status, needle):
     assert bwd_ex(**kw) == status

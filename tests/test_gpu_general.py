@@ -278,3 +278,103 @@ def test_head_dim_96_strided_rows():
     dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, causal=True, scale=scale)
     torch.cuda.synchronize()
     _check(g, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, (-1, 0), scale, "bf16", True)
+
+
+# --------------------------------------------------------- additive bias ---
+
+def _bias_case(B, H, nq, nk, d, dtype, window, seed, bias_shape, neg_inf_frac=0.0):
+    g = inputs.generate(B, H, nq, d, dtype, seed=seed, with_grad_output=True, nk=nk)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    bias = rng.standard_normal(bias_shape, dtype=np.float32) * 2.0
+    if neg_inf_frac > 0:
+        bias[rng.random(bias_shape) < neg_inf_frac] = -np.inf
+    scale = inputs.default_scale(d)
+    q, k, v, do = (to_dev(g[n]) for n in ("q", "k", "v", "do"))
+    tb = torch.from_numpy(bias).cuda()
+    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale, bias=tb)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale, bias=tb)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    b64 = bias.astype(np.float64)
+    win = _win(window)
+    ro, rl = oracle.forward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), scale, window=win, bias=b64)
+    compare("O", f64(o), ro, tol["o"], REL_FRO)
+    compare("LSE", f64(lse), rl, tol["lse"] * 4)
+    rq, rk, rv = oracle.backward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), g["do"].to_f64(), scale,
+                                 window=win, bias=b64)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        compare(name, f64(got), ref, tol["grad"] * max(1.0, float(np.abs(ref).max(initial=0.0))), REL_FRO)
+
+
+@pytest.mark.parametrize("window", [None, (-1, 0), (50, 0)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq,nk", [(130, 130), (64, 300), (301, 67)])
+def test_full_bias_fwd_bwd(nq, nk, d, dtype, window):
+    """A dense [B, H, Nq, Nk] bias on top of every mask kind; Nk a multiple of 4
+    is not required (rows are padded to 16 bytes by the test's layout)."""
+    nk4 = (nk + 3) // 4 * 4
+    B, H = 1, 2
+    # allocate rows of nk4 floats and hand over the [.., :nk] view
+    g_seed = 8000 + nq + nk + d
+    g = inputs.generate(B, H, nq, d, dtype, seed=g_seed, with_grad_output=True, nk=nk)
+    rng = np.random.Generator(np.random.PCG64(g_seed + 1))
+    full = rng.standard_normal((B, H, nq, nk4), dtype=np.float32) * 2.0
+    scale = inputs.default_scale(d)
+    q, k, v, do = (to_dev(g[n]) for n in ("q", "k", "v", "do"))
+    tb = torch.from_numpy(full).cuda()[..., :nk]
+    assert tb.stride(2) == nk4
+    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale, bias=tb)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale, bias=tb)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    b64 = full[..., :nk].astype(np.float64)
+    win = _win(window)
+    ro, rl = oracle.forward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), scale, window=win, bias=b64)
+    compare("O", f64(o), ro, tol["o"], REL_FRO)
+    compare("LSE", f64(lse), rl, tol["lse"] * 4)
+    rq, rk, rv = oracle.backward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), g["do"].to_f64(), scale,
+                                 window=win, bias=b64)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        compare(name, f64(got), ref, tol["grad"] * max(1.0, float(np.abs(ref).max(initial=0.0))), REL_FRO)
+
+
+def test_key_padding_bias_broadcast():
+    """One [B, 1, 1, Nk] row of 0 / -inf per batch (a key-padding mask),
+    broadcast over heads and queries through strides of 0."""
+    _bias_case(2, 3, 200, 260, 128, "bf16", None, 8100, (2, 1, 1, 260), neg_inf_frac=0.3)
+
+
+def test_bias_masks_whole_rows():
+    """-inf on every key of some rows: O = 0, LSE = -inf, dQ = 0 there."""
+    B, H, n, d = 1, 2, 100, 64
+    g = inputs.generate(B, H, n, d, "bf16", seed=8200, with_grad_output=True)
+    bias = np.zeros((1, 1, n, n), np.float32)
+    bias[..., 10:20, :] = -np.inf
+    tb = torch.from_numpy(bias).cuda()
+    q, k, v, do = (to_dev(g[x]) for x in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_ex(q, k, v, bias=tb)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, bias=tb)
+    torch.cuda.synchronize()
+    assert torch.all(o[:, :, 10:20] == 0) and torch.all(torch.isneginf(lse[:, :, 10:20]))
+    assert torch.all(dq[:, :, 10:20] == 0)
+    scale = inputs.default_scale(d)
+    ro, rl = oracle.forward(g["q"].to_f64(), g["k"].to_f64(), g["v"].to_f64(), scale, bias=bias.astype(np.float64))
+    compare("O", f64(o), ro, TOL["bf16"]["o"], REL_FRO)
+    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_bias_other_head_dims(d):
+    _bias_case(1, 2, 150, 152, d, "bf16", (-1, 0), 8300 + d, (1, 2, 150, 152))
+
+
+def test_zero_bias_matches_no_bias():
+    g = inputs.generate(1, 2, 333, 128, "bf16", seed=8400, with_grad_output=True)
+    q, k, v, do = (to_dev(g[x]) for x in ("q", "k", "v", "do"))
+    zero = torch.zeros(1, 1, 1, 333, dtype=torch.float32, device="cuda")
+    o0, l0 = fa.fa_fwd_ex(q, k, v, causal=True)
+    o1, l1 = fa.fa_fwd_ex(q, k, v, causal=True, bias=zero)
+    torch.cuda.synchronize()
+    assert float((o0.float() - o1.float()).abs().max()) < 1e-2
+    assert float((l0 - l1).abs().max()) < 1e-4

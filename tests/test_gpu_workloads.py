@@ -137,10 +137,13 @@ def _suite_run(name):
         q, k, v, do = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v, do))
     window = w.get("window", (-1, 0) if w["causal"] else (-1, -1))
     scale = inputs.default_scale(w["d"])
-    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale)
-    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale)
+    bias = inputs.generate_bias(w["bias"], w["seed"] + 1) if "bias" in w else None
+    tb = None if bias is None else torch.from_numpy(bias).to(dev)
+    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale, bias=tb)
+    dq, dk, dv = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale, bias=tb)
     torch.cuda.synchronize()
     win = tuple(None if x < 0 else x for x in window)
+    g["bias"] = bias
     return w, g, scale, win, (o, lse, dq, dk, dv)
 
 
@@ -151,16 +154,21 @@ def _check_suite(name, heads_fwd, heads_bwd):
     o64, l64 = f64(o), f64(lse)
     gq, gk, gv = f64(dq), f64(dk), f64(dv)
     q64, k64, v64, do64 = (g[x].to_f64() for x in ("q", "k", "v", "do"))
+    bias = g.get("bias")
+    head_bias = (lambda b, h: None) if bias is None else (lambda b, h: np.broadcast_to(
+        bias, (w["B"], w["H"]) + bias.shape[2:])[b, h].astype(np.float64))
     assert np.all(np.isfinite(o64)) and np.all(np.isfinite(gq)) and np.all(np.isfinite(gk))
     for flat in heads_fwd:
         b, h = divmod(flat, w["H"])
         rows = _sample_rows(w["N"], rng)
-        ro, rl = oracle.forward_head(q64[b, h], k64[b, h], v64[b, h], scale, rows=rows, window=win)
+        ro, rl = oracle.forward_head(q64[b, h], k64[b, h], v64[b, h], scale, rows=rows, window=win,
+                                     bias=head_bias(b, h))
         compare(f"O[{b},{h}]", o64[b, h, rows], ro, TOL[dtype]["o"], REL_FRO)
         compare(f"LSE[{b},{h}]", l64[b, h, rows], rl, TOL[dtype]["lse"])
     for flat in heads_bwd:
         b, h = divmod(flat, w["H"])
-        rq, rk, rv = oracle.backward_head(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, window=win)
+        rq, rk, rv = oracle.backward_head(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, window=win,
+                                          bias=head_bias(b, h))
         for nm, got, ref in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
             compare(f"{nm}[{b},{h}]", got[b, h], ref, TOL[dtype]["grad"] * max(1.0, float(np.abs(ref).max())),
                     REL_FRO)
@@ -202,3 +210,7 @@ def test_bnhd_n8192_equals_contiguous_bitwise():
                                                       ("d256_n8192", [0, 15], [9])])
 def test_head_dims_n8192_sampled(name, heads_fwd, heads_bwd):
     _check_suite(name, heads_fwd=heads_fwd, heads_bwd=heads_bwd)
+
+
+def test_bias_n4096_sampled():
+    _check_suite("bias_n4096_d128", heads_fwd=[0, 31], heads_bwd=[17])
