@@ -20,9 +20,13 @@
 //    barrier separates phases, so on every SIMD one wave feeds the matrix core
 //    while the other runs the softmax on the vector ALU.
 //  * Both groups use K_j and V_{j-1} during iteration j, so the two tiles are
-//    loaded together as one set, double-buffered in LDS; group A copies set
-//    j+1 global -> LDS (buffer_load ... lds, zero-fill past the end) while set
-//    j is in use.
+//    kept together as one set, double-buffered in LDS, and copied global ->
+//    LDS with buffer_load ... lds (zero-fill past the end). The copies are
+//    split between the groups: group A copies K_{j+1} at the start of its
+//    matrix phase j; group B copies V_{j+1} into set j's buffer (set j + 2)
+//    at the start of its softmax phase j, once both groups have read set j.
+//    Each copy has two phases to land, and neither group's matrix phase
+//    carries the whole copy.
 //  * Scores are computed transposed, S^T = K Q^T, with Q (the B operand) kept
 //    in registers. Each lane then holds one query's scores for 32 keys, so the
 //    row max and row sum are in-lane reductions plus one exchange across the
@@ -258,17 +262,17 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 }
 
 // One iteration j < n_tiles of the main loop (keys key_base + j * kBlockN
-// onwards): group A copies set j + 1 (K_{j+1} into `kn`, V_j into `vn`), then
-// matrix(j) on set j (K_j in `kt`, V_{j-1} in `vt`), a barrier, softmax(j),
-// the wait for this wave's copies and a barrier. The buffers are fixed per
-// call (the loop is unrolled by two) so the compiler can see that reading set
-// j never depends on the copy into the other set. Every wave runs every tile
-// of its work-group: a tile wholly outside a wave's band has all scores at
-// -inf, so its p are 0 and it changes nothing.
+// onwards): matrix(j) on set j (K_j in `kt`, V_{j-1} in `vt`), a barrier,
+// softmax(j), a barrier, with the copies placed as described at the top (K_{j+1}
+// goes to `kn`; set j + 1's V_j was copied by group B one iteration earlier).
+// The buffers are fixed per call (the loop is unrolled by two) so the compiler
+// can see that reading set j never depends on a copy into the other set. Every
+// wave runs every tile of its work-group: a tile wholly outside a wave's band
+// has all scores at -inf, so its p are 0 and it changes nothing.
 template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, bool group_b, const bf16_t* kt,
-                                              const bf16_t* vt,
-                                              bf16_t* kn, bf16_t* vn,
+                                              bf16_t* vt,
+                                              bf16_t* kn,
                                               const TileDma<32 * KB, D, kThreads / 2>& dma,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const RowRead<D>& krd, const TrRead<D>& vrd,
@@ -276,19 +280,22 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               int wq0, int qi, int lane, const float* brow) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
-  if (!group_b) {
-    if (j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
-    dma.issue(vrs, vn, key0, 2u * p.v_sr);
-  }
+  // group A copies K_{j+1} into set j + 1 during its matrix phase; group B
+  // copies V_{j+1} into set j's buffer (which becomes set j + 2) during its
+  // softmax phase, once both groups have read set j, and waits for it at the
+  // end of its next matrix phase
+  if (!group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
   matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
+  if (group_b) wait_vmem();
   __syncthreads();
+  if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
   // the wave's rows are wq0 .. wq0 + 31: the last has the highest lower
   // bound, the first the lowest upper bound
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
   softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow);
-  wait_vmem();
+  if (!group_b) wait_vmem();
   __syncthreads();
 }
 
@@ -354,6 +361,7 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   TrRead<D> vrd;
   vrd.init(lane);
   if (!group_b) dma.issue(krs, k_lds0, key_base, 2u * p.k_sr);
+  if (group_b && n_tiles > 0) dma.issue(vrs, v_lds1, key_base, 2u * p.v_sr);  // V_0 of set 1
 
   bf16x8 qf[D / 16];
   {
@@ -389,13 +397,13 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   if (group_b) __syncthreads();
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
-    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
                                   vrd, qf, st, p, wq0, qi, lane, brow);
-    fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs,
+    fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs, vrs,
                                   krd, vrd, qf, st, p, wq0, qi, lane, brow);
   }
   if (j < n_tiles)
-    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, krd,
+    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
                                   vrd, qf, st, p, wq0, qi, lane, brow);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
   pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
