@@ -271,6 +271,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 // direct-to-LDS copies) has completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Work-group barrier for hand-offs through LDS. __syncthreads() also makes
+// every wave wait for all of its outstanding global -> LDS copies (its release
+// fence counts them as LDS stores), which would cut a copy's time to land to
+// the one phase it was issued in. Here the waves wait only for their own LDS
+// reads and writes; a copy's consumer waits for it explicitly (wait_vmem in
+// the issuing wave before the barrier that hands the tile over). The memory
+// clobber keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Work-group id remap so that consecutive logical blocks (the query blocks of
 // one head) run on the same XCD and share its L2: hardware hands work-group
 // ids to the 8 XCDs round-robin.

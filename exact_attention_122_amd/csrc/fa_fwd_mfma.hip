@@ -24,9 +24,12 @@
 //    LDS with buffer_load ... lds (zero-fill past the end). The copies are
 //    split between the groups: group A copies K_{j+1} at the start of its
 //    matrix phase j; group B copies V_{j+1} into set j's buffer (set j + 2)
-//    at the start of its softmax phase j, once both groups have read set j.
-//    Each copy has two phases to land, and neither group's matrix phase
-//    carries the whole copy.
+//    at the end of its softmax phase j, once both groups have read set j and
+//    once group A's K copy of the same phase has drained (issued at the start
+//    of the phase, behind that copy, the V copy stalled group B's softmax by
+//    about a third). Each copy has a whole phase after its issue to land:
+//    the barriers wait only for LDS accesses (lds_barrier), and each group
+//    waits for its own copy just before the barrier that hands it over.
 //  * Scores are computed transposed, S^T = K Q^T, with Q (the B operand) kept
 //    in registers. Each lane then holds one query's scores for 32 keys, so the
 //    row max and row sum are in-lane reductions plus one exchange across the
@@ -107,13 +110,14 @@ struct RowState {
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// O += P_{j-1} V_{j-1}
+// O += P_{j-1} V_{j-1}. The four output blocks are interleaved, so no MFMA
+// waits on the accumulator of the one just before it.
 template <typename E, int D, int KB>
 __device__ __forceinline__ void pv_mfma(RowState<D, KB>& st, const bf16_t* vt, const TrRead<D>& vrd) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int t = 0; t < 2 * KB; ++t)
 #pragma unroll
-    for (int t = 0; t < 2 * KB; ++t) st.acc[db] = E::mfma(vrd(vt, t, db), st.pb[t], st.acc[db]);
+    for (int db = 0; db < D / 32; ++db) st.acc[db] = E::mfma(vrd(vt, t, db), st.pb[t], st.acc[db]);
 }
 
 // Matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.
@@ -280,23 +284,24 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               int wq0, int qi, int lane, const float* brow) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
-  // group A copies K_{j+1} into set j + 1 during its matrix phase; group B
-  // copies V_{j+1} into set j's buffer (which becomes set j + 2) during its
-  // softmax phase, once both groups have read set j, and waits for it at the
-  // end of its next matrix phase
+  // group A copies K_{j+1} into set j + 1 during its matrix phase and waits
+  // for it at the end of its softmax phase; group B copies V_{j+1} into set
+  // j's buffer (which becomes set j + 2) at the end of its softmax phase,
+  // once both groups have read set j, and waits for it at the end of its next
+  // matrix phase
   if (!group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
   matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
   if (group_b) wait_vmem();
-  __syncthreads();
-  if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
+  lds_barrier();
   // the wave's rows are wq0 .. wq0 + 31: the last has the highest lower
   // bound, the first the lowest upper bound
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
   softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow);
+  if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
   if (!group_b) wait_vmem();
-  __syncthreads();
+  lds_barrier();
 }
 
 // d <= 64 needs few enough registers (at most 128 per lane) for two
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   for (int i = tid; i < kBlockN * P / 8; i += kThreads) ((FA_LDS u32x4*)(FA_LDS bf16_t*)v_lds0)[i] = u32x4{};
 
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
   // Iteration j uses LDS set j % 2 = {K_j, V_{j-1}}: matrix(j) = O += P_{j-1}
   // V_{j-1} and S_j = K_j Q^T, then softmax(j). Both groups run this same
   // loop, group B one phase (one barrier) behind group A, so while one group
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   // set j + 1 during its iteration j (phases 2j and 2j + 1); set j is last
   // read by group B in phase 2j + 1, and set j + 1 is first read by group A in
   // phase 2j + 2.
-  if (group_b) __syncthreads();
+  if (group_b) lds_barrier();
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
     fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
                                   vrd, qf, st, p, wq0, qi, lane, brow);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
   pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
-  if (!group_b) __syncthreads();
+  if (!group_b) lds_barrier();
 
   // epilogue: O = acc / l, LSE = m * |scale| + ln l (-inf for a row with no key)
   const float lt = pair_sum(st.l);
