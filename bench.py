@@ -263,15 +263,21 @@ def main():
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     f_fwd = attention_flops(B, H, N, d, causal)
     f_bwd = 2.5 * f_fwd
+    # algorithmic HBM bytes (bf16): forward reads Q, K, V and writes O, LSE;
+    # backward reads Q, K, V, O, dO, LSE and writes dQ, dK, dV
+    fwd_bytes = B * H * (4 * N * d * 2 + N * 4)
+    bwd_bytes = B * H * (8 * N * d * 2 + N * 4)
     res = {}
     res["fwd"] = {"ms": round(fwd_avg, 4), "tflops": round(f_fwd / fwd_avg / 1e9, 2),
-                  "frac_peak": round(f_fwd / fwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                  "frac_peak": round(f_fwd / fwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                  "hbm_GBps": round(fwd_bytes / fwd_avg / 1e6, 1)}
     step_flops = f_fwd
     if not args.fwd_only:
         bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
         bwd_avg = sum(bwd_ms) / len(bwd_ms)
         res["bwd"] = {"ms": round(bwd_avg, 4), "tflops": round(f_bwd / bwd_avg / 1e9, 2),
-                      "frac_peak": round(f_bwd / bwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                      "frac_peak": round(f_bwd / bwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      "hbm_GBps": round(bwd_bytes / bwd_avg / 1e6, 1)}
         step_flops += f_bwd
     value = step_flops / ms_per_step / 1e9   # TFLOP/s
 
@@ -281,7 +287,7 @@ def main():
     roof = {"kernel": f"{kname} (fa_fwd)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),
-            "algorithmic_bytes": B * H * (4 * N * d * 2 + N * 4)}
+            "algorithmic_bytes": fwd_bytes}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
