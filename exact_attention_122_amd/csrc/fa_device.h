@@ -154,28 +154,36 @@ struct Swz {
 //           column 32 db + lane % 32: with read 0 at rows +{0..3} and read 1
 //           at rows +{8..11}, lane l receives a 32x16 A operand whose k index
 //           runs over rows in the order the score accumulators hold them.
+// With 32 or more chunks per row the swizzle only changes the low four bits
+// of a chunk index, so the offsets of chunks 16 .. 31 are those of chunks
+// 0 .. 15 plus 256 bytes: only the first 16 chunks' offsets are kept in
+// registers (at d = 256 this frees 16 registers per lane), and the rest is a
+// constant folded into the instruction.
 template <int D>
 struct RowRead {
   static constexpr int P = lds_pitch<D>();
-  uint32_t off[D / 16];
+  static constexpr int kOff = D / 16 > 8 ? 8 : D / 16;  // operand steps of the first 16 chunks
+  uint32_t off[kOff];
   __device__ __forceinline__ void init(int lane) {
     const int row = lane & 31, hw = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(row * P + (Swz<P>::chunk(row, 2 * ks + hw) << 3)) * 2;
+    for (int ks = 0; ks < kOff; ++ks) off[ks] = (uint32_t)(row * P + (Swz<P>::chunk(row, 2 * ks + hw) << 3)) * 2;
   }
   __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int kb, int ks) const {
-    return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks] + kb * 32 * P * 2);
+    return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks % kOff] +
+                                   (ks / kOff) * 256 + kb * 32 * P * 2);
   }
 };
 
 template <int D>
 struct TrRead {
   static constexpr int P = lds_pitch<D>();
-  uint32_t off[D / 32][2];
+  static constexpr int kOff = D / 32 > 4 ? 4 : D / 32;  // output blocks of the first 16 chunks
+  uint32_t off[kOff][2];
   __device__ __forceinline__ void init(int lane) {
     const int s = lane & 15, hw = lane >> 5;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < kOff; ++db)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = 4 * hw + (s >> 2) + 8 * i;
@@ -185,9 +193,9 @@ struct TrRead {
   }
   // rows t * 16 + ... (f(row) only depends on row % 16, so +16 rows is a constant)
   __device__ __forceinline__ bf16x8 operator()(const bf16_t* tile, int t, int db) const {
-    const FA_LDS char* base = (const FA_LDS char*)(const FA_LDS bf16_t*)tile + t * 16 * P * 2;
-    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][0]));
-    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db][1]));
+    const FA_LDS char* base = (const FA_LDS char*)(const FA_LDS bf16_t*)tile + t * 16 * P * 2 + (db / kOff) * 256;
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db % kOff][0]));
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off[db % kOff][1]));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8, z);
