@@ -205,7 +205,7 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path: heads are independent and would shard with no exchange.", file=sys.stderr)
         sys.exit(2)
     if args.suite:
