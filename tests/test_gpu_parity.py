@@ -149,6 +149,30 @@ def test_fwd_is_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, False), (256, False)])
+def test_fwd_repeated_launches_bitwise(d, causal):
+    """Ten back-to-back launches on a grid that fills every CU, each equal bit for
+    bit to the first: a tile read before its global -> LDS copy has landed, or
+    a copy that overwrites a tile still being read, would show up as launches
+    that differ."""
+    B, H, N = 1, 32, 2048 if d == 256 else 4096
+    g = inputs.generate(B, H, N, d, "bf16", seed=5100 + d + causal)
+    q, k, v = (to_dev(g[x]) for x in ("q", "k", "v"))
+    scale = inputs.default_scale(d)
+    outs = []
+    for _ in range(10):
+        outs.append(fa.fa_fwd(q, k, v, causal=causal, scale=scale))
+    torch.cuda.synchronize()
+    o0, l0 = outs[0]
+    for o, lse in outs[1:]:
+        assert torch.equal(o, o0) and torch.equal(lse, l0)
+    # and the first launch is right: sampled rows against the oracle
+    rows = np.array([0, 1, 255, 256, 1000, N - 1])
+    ro, rl = oracle.forward(g["q"].to_f64()[:, :2], g["k"].to_f64()[:, :2], g["v"].to_f64()[:, :2], scale, causal)
+    compare("O", f64(o0[:, :2])[:, :, rows], ro[:, :, rows], TOL["bf16"]["o"])
+    compare("LSE", f64(l0[:, :2])[:, :, rows], rl[:, :, rows], TOL["bf16"]["lse"])
+
+
 def test_bwd_is_bitwise_deterministic():
     g = inputs.generate(1, 2, 256, 64, "bf16", seed=4800, with_grad_output=True)
     q, k, v, o, lse = gpu_fwd(g, False, 0.125)
