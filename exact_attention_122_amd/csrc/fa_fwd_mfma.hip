@@ -56,7 +56,9 @@
 //  * An optional fp32 bias is added to the scaled scores. Its kernels work in
 //    log2 units from the start (y = c s + log2(e) bias, one FMA) instead of
 //    raw score units, and each lane loads the bias of its query row, four
-//    consecutive keys per 16-byte load.
+//    consecutive keys per 16-byte load, at the start of the matrix phase that
+//    precedes the softmax phase using it (64-key tiles make room for it in
+//    the registers), so the load latency hides behind the MFMAs.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -68,11 +70,21 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per work-group
 
 // 32-key blocks per K/V tile: 128 keys where the registers allow long
-// phases, 64 at small d (two work-groups per CU share the registers), 32 at
-// d = 256 (the O accumulators alone take half the registers)
-template <int D>
+// phases, 64 at small d (two work-groups per CU share the registers) and
+// with a bias (whose values for the tile are held in registers through the
+// matrix phase), 32 at d = 256 (the O accumulators alone take half the
+// registers)
+template <int D, bool BIAS>
 constexpr int key_blocks() {
-  return D >= 256 ? 1 : D >= 96 ? 4 : 2;
+  return D >= 256 ? 1 : (D >= 96 && !BIAS) ? 4 : 2;
+}
+
+// Whether a bias kernel reads its tile's bias at the start of the matrix
+// phase (its latency then hides behind the MFMAs) rather than in the softmax
+// phase that adds it; d = 256 has no registers to hold it that long.
+template <int D, bool BIAS>
+constexpr bool bias_ahead() {
+  return BIAS && D < 256;
 }
 
 struct FwdParams {
@@ -160,12 +172,25 @@ __device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* 
   for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
 }
 
+// Bias of keys kc .. kc + 3 of this lane's query row (zeros past the last key).
+__device__ __forceinline__ f32x4 load_bias4(const float* brow, int kc, int nk) {
+  f32x4 bv = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kc + 3 < nk) {
+    bv = *(const f32x4*)(brow + kc);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      if (kc + rr < nk) bv[rr] = brow[kc + rr];
+  }
+  return bv;
+}
+
 // Softmax phase for the tile whose scores are in st.s. With a bias the scores
 // become y = c s + log2(e) bias (log2 units) first; `masked` tiles (band
 // edges, ragged end) then set the scores of dead keys to -inf.
 template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
-                                              bool masked, const float* brow) {
+                                              bool masked, const float* brow, const f32x4 (&bpre)[4 * KB]) {
   constexpr int kN = 16 * KB;  // scores per lane
   const int hw = lane >> 5;
   // scale of the working units: raw scores without bias, log2 units with one
@@ -181,19 +206,15 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
     for (int b = 0; b < KB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int kc = key0 + 32 * b + 8 * g + 4 * hw;  // keys kc .. kc + 3 of registers 4 g .. 4 g + 3
-        f32x4 bv = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kc + 3 < p.nk) {
-          bv = *(const f32x4*)(brow + kc);
-        } else {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (kc + rr < p.nk) bv[rr] = brow[kc + rr];
-        }
+        f32x4 bv;
+        if constexpr (bias_ahead<D, BIAS>())
+          bv = bpre[4 * b + g];
+        else
+          bv = load_bias4(brow, key0 + 32 * b + 8 * g + 4 * hw, p.nk);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[16 * b + 4 * g + rr] = fmaf(x[16 * b + 4 * g + rr], p.c, kLog2e * bv[rr]);
-        // one key block's loads at a time: the bias must not take 16 KB x 4
-        // of registers beside the scores
+        // (loads here at d = 256 only) one key block's loads at a time: the
+        // bias must not take more registers beside the scores
         if (g == 3) __builtin_amdgcn_sched_barrier(0);
       }
   }
@@ -284,6 +305,17 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               int wq0, int qi, int lane, const float* brow) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
+  // the bias of this tile, for the softmax phase after the matrix phase: read
+  // now, so its latency hides behind the matrix phase (and ahead of the tile
+  // copy, so waiting for it never waits for the copy)
+  f32x4 bpre[4 * KB];
+  if constexpr (bias_ahead<D, BIAS>()) {
+    const int hw = lane >> 5;
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bpre[4 * b + g] = load_bias4(brow, key0 + 32 * b + 8 * g + 4 * hw, p.nk);
+  }
   // group A copies K_{j+1} into set j + 1 during its matrix phase and waits
   // for it at the end of its softmax phase; group B copies V_{j+1} into set
   // j's buffer (which becomes set j + 2) at the end of its softmax phase,
@@ -298,7 +330,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
-  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow);
+  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow, bpre);
   if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
   if (!group_b) wait_vmem();
   lds_barrier();
@@ -314,7 +346,7 @@ constexpr int fwd_blocks_per_cu() {
 template <typename E, int D, int MASK, bool BIAS>
 __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(FwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
-  constexpr int KB = key_blocks<D>();
+  constexpr int KB = key_blocks<D, BIAS>();
   constexpr int kBlockN = 32 * KB;  // keys per tile
   constexpr int P = lds_pitch<D>();
   // Two sets of (K tile, V tile), declared as separate objects so the compiler
