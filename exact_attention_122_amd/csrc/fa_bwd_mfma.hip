@@ -132,6 +132,17 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
                                           float c, int q0, int q_lo, int q_hi, int lane, bool masked,
                                           const float* bcol, long long bias_sr, int nq) {
   const int hw = lane >> 5;
+  // The tile's bias down this lane's key column, read before the S/dP
+  // products so that its latency hides behind them (read next to its use, it
+  // stalled every tile on memory latency). d = 256 has no registers for it.
+  float bpre[32];
+  if constexpr (BIAS && D <= 128) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int qr = q0 + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * hw + (i & 3);
+      bpre[i] = (bcol && qr < nq) ? bcol[qr * bias_sr] : 0.f;
+    }
+  }
   f32x16 s[2], dp[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -159,8 +170,12 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
         float arg = fmaf(s[qb][i], c, -Lv[rr]);
         if constexpr (BIAS) {
           // bias[q][key] down this lane's key column (bcol is null past the last key)
-          const int qr = q0 + r0 + rr;
-          if (bcol && qr < nq) arg = fmaf(kLog2e, bcol[qr * bias_sr], arg);
+          if constexpr (D <= 128) {
+            arg = fmaf(kLog2e, bpre[qb * 16 + i], arg);
+          } else {
+            const int qr = q0 + r0 + rr;
+            if (bcol && qr < nq) arg = fmaf(kLog2e, bcol[qr * bias_sr], arg);
+          }
         }
         if (MASK != kMaskNone && masked) {
           const int qr = q0 + r0 + rr;
