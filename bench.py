@@ -50,9 +50,12 @@ def fwd_source_sha256():
     return h.hexdigest()
 
 
+TRAFFIC_WORKLOAD = "fwd_n8192_d128"   # the workload the counter passes ran
+
+
 def measured_traffic(kernel):
-    """Counter-derived HBM bytes per launch of `kernel`, or None if not measured
-    for the current sources."""
+    """Counter-derived HBM bytes per launch of `kernel` on TRAFFIC_WORKLOAD, or
+    None if not measured for the current sources."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -286,7 +289,8 @@ def main():
     kname = f"fwd_kernel<bf16,{d},{'upper' if causal else 'none'}>"
     roof = {"kernel": f"{kname} (fa_fwd)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(kname) if args.workload == TRAFFIC_WORKLOAD else None,
             "algorithmic_bytes": fwd_bytes}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
