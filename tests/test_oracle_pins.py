@@ -415,14 +415,41 @@ def test_bias_broadcasts_over_heads_in_the_batched_oracle():
 
 @pytest.mark.parametrize("block", [1, 3, 7, 16, 64, 100])
 @pytest.mark.parametrize("causal", [False, True])
-def test_online_softmax_replay_equals_full_softmax(block, causal):
+@pytest.mark.parametrize("order", ["sequential", "tree"])
+def test_online_softmax_replay_equals_full_softmax(block, causal, order):
     n, d = 100, 16
     q, k, v = _rand((n, d), 33), _rand((n, d), 34), _rand((n, 12), 35)
     o_full, l_full = oracle.forward_head(q, k, v, 0.25, causal)
     o_rep, l_rep = orp.online_softmax_attention(q, k, v, 0.25, orp.partition_keys(n, block),
-                                                causal=causal)
+                                                causal=causal, order=order)
     np.testing.assert_allclose(o_rep, o_full, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(l_rep, l_full, rtol=1e-12, atol=1e-13)
+
+
+def test_block_pair_merge_is_associative_commutative_with_empty_identity():
+    """The algebra the replay rests on, checked directly on three key blocks:
+    (A+B)+C = A+(B+C) = C+(A+B), the empty pair changes nothing, and a row
+    hidden from a block contributes its empty pair."""
+    rng = np.random.default_rng(7)
+    q, k, v = rng.standard_normal((6, 4)), rng.standard_normal((9, 4)), rng.standard_normal((9, 3))
+    vis = np.ones((6, 3), dtype=bool)
+    a, b, c = (orp.block_pair(q, k[i:i + 3], v[i:i + 3], 0.7, vis) for i in (0, 3, 6))
+    left = orp.merge(orp.merge(a, b), c)
+    right = orp.merge(a, orp.merge(b, c))
+    swapped = orp.merge(c, orp.merge(b, a))
+    full = orp.block_pair(q, k, v, 0.7, np.ones((6, 9), dtype=bool))
+    for x in (left, right, swapped):
+        np.testing.assert_allclose(x[0], full[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(x[1], full[1], rtol=1e-13, atol=1e-14)
+    empty = (np.zeros((6, 3)), np.full(6, -np.inf))
+    e = orp.merge(empty, a)
+    np.testing.assert_array_equal(e[0], a[0])
+    np.testing.assert_array_equal(e[1], a[1])
+    hidden = orp.block_pair(q, k[:3], v[:3], 0.7, np.zeros((6, 3), dtype=bool))
+    np.testing.assert_array_equal(hidden[0], 0.0)
+    assert np.all(np.isneginf(hidden[1]))
+    both = orp.merge(hidden, hidden)
+    assert np.all(np.isneginf(both[1])) and np.all(both[0] == 0.0)
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -438,9 +465,10 @@ def test_replay_random_partitions_and_rising_max(seed):
     if seed % 2:
         blocks = blocks[::-1]                     # order does not matter (exact maths)
     o_full, l_full = oracle.forward_head(q, k, v, 0.5)
-    o_rep, l_rep = orp.online_softmax_attention(q, k, v, 0.5, blocks)
-    np.testing.assert_allclose(o_rep, o_full, rtol=1e-12, atol=1e-12)
-    np.testing.assert_allclose(l_rep, l_full, rtol=1e-12, atol=1e-12)
+    for order in ("sequential", "tree"):
+        o_rep, l_rep = orp.online_softmax_attention(q, k, v, 0.5, blocks, order=order)
+        np.testing.assert_allclose(o_rep, o_full, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l_rep, l_full, rtol=1e-12, atol=1e-12)
 
 
 # --------------------------------------- independent library special case ---
