@@ -186,20 +186,73 @@ def calibrate_copy(mib):
 
 
 def cpu_baseline(g, w, scale, causal, heads):
-    """The fp64 oracle on a bounded sample: `heads` whole heads, fwd + bwd."""
-    import numpy as np
+    """The fp64 oracle on a bounded sample: the first `heads` (b, h) heads,
+    forward + backward. Returns the timing record and the oracle's outputs
+    (O, LSE, dQ, dK, dV) for those heads, flattened to [heads, ...]."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    q, k, v, do = (g[x].to_f64()[0, :heads] for x in ("q", "k", "v", "do"))
+    q, k, v, do = (g[x].to_f64().reshape((-1,) + g[x].shape[2:])[:heads] for x in ("q", "k", "v", "do"))
     t0 = time.perf_counter()
-    oracle.forward(q, k, v, scale, causal, workers=cores)
-    oracle.backward(q, k, v, do, scale, causal, workers=cores)
+    o, lse = oracle.forward(q, k, v, scale, causal, workers=cores)
+    dq, dk, dv = oracle.backward(q, k, v, do, scale, causal, workers=cores)
     dt = time.perf_counter() - t0
     flops = attention_flops(1, heads, w["N"], w["d"], causal) * 3.5
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{heads} of {w['B'] * w['H']} heads, forward + backward, fp64 numpy "
-                      f"(S materialised row-chunk by row-chunk), same input bytes"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "seconds": round(dt, 3),
+           "sample": f"{heads} of {w['B'] * w['H']} heads, forward + backward, fp64 numpy "
+                     f"(S materialised row-chunk by row-chunk), same input bytes"}
+    return rec, {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
+
+
+def parity(gpu, ref, heads):
+    """Max-abs and relative Frobenius error of each GPU output against the
+    oracle's, over the first `heads` heads, with the bound each must meet."""
+    import numpy as np
+    bounds = {"O": 2e-2, "LSE": 1e-3, "dQ": 2e-2, "dK": 2e-2, "dV": 2e-2}
+    out = {}
+    for name, r in ref.items():
+        t = gpu[name]
+        x = t.detach().float().cpu().numpy().astype(np.float64)
+        x = x.reshape((-1,) + x.shape[2:])[:heads]
+        diff = x - r
+        err = float(np.abs(diff).max())
+        fro = float(np.linalg.norm(diff) / np.linalg.norm(r))
+        out[name] = {"max_abs": float(f"{err:.4g}"), "rel_fro": float(f"{fro:.4g}"), "bound": bounds[name],
+                     "ok": bool(err <= bounds[name] and (name == "LSE" or fro <= 2e-2))}
+    out["heads"] = heads
+    out["all_ok"] = all(v["ok"] for k, v in out.items() if isinstance(v, dict))
+    return out
+
+
+def percentiles(ms):
+    """mean, median, p10 and p90 of per-launch times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def provenance():
+    """The git commit when the repository's history is present (it is not
+    copied everywhere the bench runs), and a SHA-256 of the library's sources
+    and this file, which identifies the code either way."""
+    import subprocess
+    head = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            head = r.stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_122_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    for path in (os.path.join(ROOT, "include", "fa.h"), os.path.abspath(__file__)):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return {"git_head": head, "source_sha256": h.hexdigest()}
 
 
 def main():
@@ -262,29 +315,34 @@ def main():
 
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
     f_fwd = attention_flops(B, H, N, d, causal)
     f_bwd = 2.5 * f_fwd
     # algorithmic HBM bytes (bf16): forward reads Q, K, V and writes O, LSE;
     # backward reads Q, K, V, O, dO, LSE and writes dQ, dK, dV
     fwd_bytes = B * H * (4 * N * d * 2 + N * 4)
     bwd_bytes = B * H * (8 * N * d * 2 + N * 4)
-    res = {}
-    res["fwd"] = {"ms": round(fwd_avg, 4), "tflops": round(f_fwd / fwd_avg / 1e9, 2),
-                  "frac_peak": round(f_fwd / fwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4),
-                  "hbm_GBps": round(fwd_bytes / fwd_avg / 1e6, 1)}
+
+    def summary(ms, flops, nbytes):
+        # rates at the mean launch time; the median and the 10th / 90th
+        # percentiles of the per-launch times show the spread
+        pc = percentiles(ms)
+        return {"ms": round(pc["mean"], 4), "ms_median": round(pc["median"], 4),
+                "ms_p10": round(pc["p10"], 4), "ms_p90": round(pc["p90"], 4),
+                "tflops": round(flops / pc["mean"] / 1e9, 2),
+                "tflops_median": round(flops / pc["median"] / 1e9, 2),
+                "frac_peak": round(flops / pc["mean"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+                "hbm_GBps": round(nbytes / pc["mean"] / 1e6, 1)}
+
+    res = {"fwd": summary([e[0].elapsed_time(e[1]) for e in evs], f_fwd, fwd_bytes)}
+    fwd_avg = res["fwd"]["ms"]
     step_flops = f_fwd
     if not args.fwd_only:
-        bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-        bwd_avg = sum(bwd_ms) / len(bwd_ms)
-        res["bwd"] = {"ms": round(bwd_avg, 4), "tflops": round(f_bwd / bwd_avg / 1e9, 2),
-                      "frac_peak": round(f_bwd / bwd_avg / 1e9 / PEAK_BF16_TFLOPS, 4),
-                      "hbm_GBps": round(bwd_bytes / bwd_avg / 1e6, 1)}
+        res["bwd"] = summary([e[1].elapsed_time(e[2]) for e in evs], f_bwd, bwd_bytes)
         step_flops += f_bwd
     value = step_flops / ms_per_step / 1e9   # TFLOP/s
 
-    # roofline of fa_fwd's kernel: algorithmic FLOPs per launch / event-timed launch duration
+    # roofline of fa_fwd's kernel: algorithmic FLOPs per launch / its mean
+    # event-timed launch duration
     ach = f_fwd / fwd_avg / 1e9
     kname = f"fwd_kernel<bf16,{d},{'upper' if causal else 'none'}>"
     roof = {"kernel": f"{kname} (fa_fwd)",
@@ -301,15 +359,20 @@ def main():
                                f"{'causal' if causal else 'non-causal'}, step = fa_fwd + fa_bwd"
                                + (" (fwd only)" if args.fwd_only else ""),
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "seed": w["seed"],
-                   "scale": scale},
+                   "scale": scale,
+                   "inputs_sha256": {x: g[x].sha256 for x in ("q", "k", "v", "do")}},
         **res,
         "frac_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "device": torch.cuda.get_device_name(dev),
         "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
+        **provenance(),
     }
     if not args.no_cpu_baseline and not args.fwd_only:
-        out["cpu_baseline"] = cpu_baseline(g, w, scale, causal, min(args.cpu_heads, B * H))
+        heads = min(args.cpu_heads, B * H)
+        out["cpu_baseline"], ref = cpu_baseline(g, w, scale, causal, heads)
+        # the outputs of the last timed step against the oracle's
+        out["parity"] = parity({"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}, ref, heads)
     print(json.dumps(out), flush=True)
 
 

@@ -1,8 +1,25 @@
 """Helpers shared by the GPU parity tests: run the HIP path through the C ABI,
 compare with the fp64 oracle element by element."""
+import json
+import os
+
 import numpy as np
 
 from exact_attention_122_amd import fa, inputs
+
+# When FA_PARITY_LOG names a file, every comparison appends one JSON line to
+# it (test, output, measured max-abs and relative Frobenius errors, bound), so
+# a run records the errors it measured and not only that they passed.
+_LOG = os.environ.get("FA_PARITY_LOG")
+
+
+def _log(name, err, fro, atol, rel, n):
+    if not _LOG:
+        return
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "output": name,
+           "max_abs": err, "rel_fro": fro, "atol": atol, "rel_bound": rel, "elements": int(n)}
+    with open(_LOG, "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 # Tolerances (max abs error vs the fp64 oracle). bf16 inputs, fp32 accumulation:
 # O and dQ/dK/dV 2e-2, LSE 1e-3; float32 end to end: 1e-5 on O and LSE.
@@ -39,13 +56,15 @@ def compare(name, got, ref, atol, rel=None):
         assert np.all(np.isneginf(got[dead])), f"{name}: expected -inf where no key is visible"
         got, ref = got[~dead], ref[~dead]
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    diff = got - ref
+    err = float(np.abs(diff).max()) if got.size else 0.0
+    den = float(np.linalg.norm(ref)) if got.size else 0.0
+    fro = float(np.linalg.norm(diff) / den) if den > 0 else None
+    del diff
+    _log(name, err, fro, atol, rel, got.size)
     assert err <= atol, f"{name}: max abs err {err:.3e} > {atol:.1e}"
-    if rel is not None and got.size:
-        den = np.linalg.norm(ref)
-        if den > 0:
-            fro = float(np.linalg.norm(got - ref) / den)
-            assert fro <= rel, f"{name}: relative Frobenius err {fro:.3e} > {rel:.1e}"
+    if rel is not None and fro is not None:
+        assert fro <= rel, f"{name}: relative Frobenius err {fro:.3e} > {rel:.1e}"
     return err
 
 
