@@ -90,8 +90,9 @@ def test_fwd_bwd_unusual_scales(scale, causal):
     q, k, v, o, lse = gpu_fwd(g, causal, scale)
     ro, rl = _oracle_fwd(g, scale, causal)
     compare("O", f64(o), ro, TOL["bf16"]["o"], REL_FRO)
-    # LSE grows with |scale|; keep the 1e-3 bound relative to the score scale
-    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"] * max(1.0, abs(scale) / 0.0884))
+    # LSE is summed in fp32 from fp32 probabilities: the 1e-3 bound holds at
+    # every scale (measured below 1e-5 at scale 1)
+    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
     do = to_dev(g["do"])
     dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
     torch.cuda.synchronize()
@@ -122,7 +123,7 @@ def test_fwd_adversarial_rescale(kind, causal):
     _, _, _, o, lse = gpu_fwd(g, causal, scale)
     ro, rl = _oracle_fwd(g, scale, causal)
     compare("O", f64(o), ro, TOL["bf16"]["o"], REL_FRO)
-    compare("LSE", f64(lse), rl, 4 * TOL["bf16"]["lse"])
+    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
 
 
 def test_constant_v_and_identical_keys_on_gpu():
