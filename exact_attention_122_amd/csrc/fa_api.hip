@@ -222,11 +222,13 @@ size_t workspace_bytes(const Problem& pr) {
   return fa::bwd_workspace_bytes(pr.bh, pr.nq);
 }
 
-// Shared body of fa_bwd and fa_bwd_ex.
+// Shared body of fa_bwd, fa_bwd_ex and fa_bwd_noalloc. With use_scratch the
+// workspace arguments are ignored: after every other check, the statistics go
+// to the library's own device scratch (kScratchBytes at most).
 int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
              void* dK, void* dV, const Problem& pr, const long long* const strides[8], const float* bias,
              const long long* bias_strides, float scale, int wl, int wr, void* workspace,
-             size_t workspace_bytes_given, void* stream) {
+             size_t workspace_bytes_given, void* stream, bool use_scratch = false) {
   int st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if ((st = check_window(wl, wr)) != FA_OK) return st;
@@ -242,15 +244,22 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     if ((st = describe(outs[i], strides[5 + i], pr, true)) != FA_OK) return st;
   const size_t need = workspace_bytes(pr);
   Extent lse{}, ws{};
+  if (use_scratch && need > fa::kScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "the problem needs %zu bytes of row statistics, more than the %zu-byte scratch of fa_bwd_noalloc "
+                "(B*H*ceil(N/64)*64 must be at most %zu): use fa_bwd with a workspace",
+                need, fa::kScratchBytes, fa::kScratchBytes / 8);
   if (pr.nq > 0) {
     if (!LSE) return fail(FA_ERR_INVALID_ARGUMENT, "LSE is NULL");
     if (!aligned16(LSE)) return fail(FA_ERR_INVALID_ARGUMENT, "LSE is not 16-byte aligned");
-    if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL");
-    if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
     lse = Extent{reinterpret_cast<uintptr_t>(LSE), reinterpret_cast<uintptr_t>(LSE) + (uintptr_t)(pr.bh * pr.nq * 4)};
-    ws = Extent{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (!use_scratch) {
+      if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+      if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+      ws = Extent{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    }
   }
-  if (workspace_bytes_given < need)
+  if (!use_scratch && workspace_bytes_given < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes_given,
                 need);
   fa::Strides sbias;
@@ -266,6 +275,13 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     for (int j = i + 1; j < 4; ++j)
       if (overlap(*out_ext[i], *out_ext[j]))
         return fail(FA_ERR_INVALID_ARGUMENT, "%s overlaps %s", out_name[i], out_name[j]);
+  }
+
+  if (use_scratch && need > 0) {
+    // the library's own device memory (a distinct symbol, so it overlaps no
+    // caller buffer); its address is looked up once per device
+    int e;
+    if ((e = hip_status(fa::scratch_address(&workspace), "scratch lookup")) != FA_OK) return e;
   }
 
   fa::BwdArgs a;
@@ -347,6 +363,19 @@ FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
   const long long* const none[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, none, nullptr, nullptr, scale, -1, causal ? 0 : -1, workspace,
                   workspace_bytes, stream);
+}
+
+FA_EXPORT int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d, float scale,
+                             int causal, int dtype, void* stream) {
+  g_detail[0] = '\0';
+  Problem pr;
+  int st = check_dims(B, H, N, N, d, dtype, &pr);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  const long long* const none[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, pr, none, nullptr, nullptr, scale, -1, causal ? 0 : -1, nullptr, 0,
+                  stream, true);
 }
 
 FA_EXPORT int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,

@@ -35,7 +35,42 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+#include <mutex>
+
 namespace fa {
+
+// Device scratch of the entry point that allocates nothing: the per-row
+// statistics live here instead of in a caller's workspace. Each GPU holds its
+// own copy from the library's load until the process ends. In host code the
+// name is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = addr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = 256;

@@ -77,4 +77,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a);  // bf16 and fp16
 // Workspace of the backward: two floats per query row, rows padded to 64 per head.
 size_t bwd_workspace_bytes(long long bh, int nq);
 
+// Size of the library's own device scratch (the backward's workspace for the
+// entry point that allocates nothing), and its address on the current device
+// (looked up once per device; every call on a device shares it).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_address(void** out);
+
 }  // namespace fa

@@ -26,7 +26,9 @@ FA_FP16 = 2
 
 EXPORTS = ("fa_version", "fa_status_string", "fa_last_error_detail", "fa_fwd",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex_workspace_bytes",
-           "fa_bwd_ex")
+           "fa_bwd_ex", "fa_bwd_noalloc")
+# bytes of the device scratch fa_bwd_noalloc uses (FA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -54,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lp = ctypes.POINTER(ctypes.c_longlong)
     lib.fa_fwd_ex.restype = i
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, lp, lp, lp, lp, vp, lp, f, i, i, i, vp]
@@ -172,6 +176,29 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None
                                dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
                                workspace.data_ptr(), workspace.numel(), _stream(q))
     _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+                   dq=None, dk=None, dv=None):
+    """fa_bwd without a workspace: the library's own per-GPU scratch holds the
+    row statistics (see include/fa.h). Pass dq, dk, dv to allocate nothing."""
+    import torch
+    _same(q, k, v, o, do)
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = default_scale(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _same(q, dq, dk, dv)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise RuntimeError("lse must be a contiguous float32 [B, H, N] tensor")
+    st = load_library().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                       _dtype_code(q), _stream(q))
+    _check(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

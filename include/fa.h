@@ -21,7 +21,8 @@
  *    log-sum-exp of the scaled scores of each query row.
  *  - Every tensor pointer is a DEVICE pointer (memory of the current HIP
  *    device). Base pointers must be 16-byte aligned. The caller allocates and
- *    owns every buffer; the library allocates, frees and retains nothing.
+ *    owns every buffer; the library allocates, frees and retains nothing
+ *    (fa_bwd_noalloc's fixed per-GPU scratch aside, see there).
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; outputs are valid once the stream reaches that point and
  *    inputs must stay unchanged until then.
@@ -41,7 +42,8 @@
  *    request the kernels do not cover returns FA_ERR_UNSUPPORTED; there is
  *    never a silent fallback to a different implementation. After an error,
  *    fa_last_error_detail() (thread-local) explains it.
- *  - The functions are thread-safe and keep no state between calls.
+ *  - The functions are thread-safe and keep no state between calls, except
+ *    fa_bwd_noalloc, whose calls share one scratch array per GPU.
  */
 #ifndef EXACT_ATTENTION_FA_H
 #define EXACT_ATTENTION_FA_H
@@ -124,6 +126,38 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Size of the device scratch that fa_bwd_noalloc uses in place of a
+ * workspace: 16 MiB per GPU, i.e. B*H*ceil(N/64)*64 <= 2097152 padded query
+ * rows (for example 64 heads of N = 32768, or 32 heads of N = 65536).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, definition and results as fa_bwd (bit for bit), minus the
+ * workspace: the per-row statistics go to a scratch array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on, from
+ * its load until the process ends. The call allocates and frees nothing
+ * (no hipMalloc, no library routine that allocates). The caller still owns
+ * every input and output.
+ *
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * contents (the backward overwrites every entry it reads, so no clearing is
+ * needed). Calls that overlap in time on one GPU (different streams or host
+ * threads without ordering between them) race on it and give undefined
+ * results; order them on one stream or use fa_bwd with separate workspaces.
+ *
+ * Errors: as fa_bwd; a problem with B*H*ceil(N/64)*64*8 bytes of statistics
+ * above FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_UNSUPPORTED before any HIP
+ * call.
+ */
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, void* dQ, void* dK,
+                   void* dV, int B, int H, int N, int d, float scale,
+                   int causal, int dtype, void* stream);
 
 /*
  * fa_fwd for general shapes, layouts and masks: Nq queries over Nk keys, a

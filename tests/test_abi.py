@@ -106,6 +106,39 @@ def test_bwd_empty_problem_is_a_no_op():
     assert bwd(N=0, ptrs=[0] * 9, ws=0, ws_bytes=0) == fa.FA_OK
 
 
+def noalloc(*, ptrs=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16):
+    lib = fa.load_library()
+    ptrs = ptrs or P[:9]
+    return lib.fa_bwd_noalloc(*ptrs, B, H, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    # statistics of 33 heads x 65536 rows (17.3 MB) exceed the 16 MiB scratch
+    (dict(H=33, N=65536, d=128), fa.FA_ERR_UNSUPPORTED, "scratch"),
+    (dict(ptrs=[0] + P[1:9]), fa.FA_ERR_INVALID_ARGUMENT, "Q is NULL"),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16"),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(ptrs=P[:6] + [P[0], P[7], P[8]]), fa.FA_ERR_INVALID_ARGUMENT, "overlaps"),
+])
+def test_bwd_noalloc_rejects_on_the_host(kw, status, needle):
+    """Every check runs before the scratch lookup or any launch."""
+    assert noalloc(**kw) == status
+    assert needle in fa.fa_last_error_detail()
+
+
+def test_bwd_noalloc_largest_accepted_problem_fits_the_scratch():
+    assert fa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # 32 heads of 65536 rows is exactly the scratch; validation then needs
+    # real pointers, so only the size arithmetic is checked here
+    assert fa.fa_bwd_workspace_bytes(1, 32, 65536, 128) == fa.NOALLOC_SCRATCH_BYTES
+    assert fa.fa_bwd_workspace_bytes(1, 33, 65536, 128) > fa.NOALLOC_SCRATCH_BYTES
+
+
+def test_bwd_noalloc_empty_problem_is_a_no_op():
+    assert noalloc(N=0, ptrs=[0] * 9) == fa.FA_OK
+
+
 def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 8
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 64 * 8
