@@ -165,6 +165,9 @@ int describe_bias(const float* bias, const long long* strides, const Problem& pr
   if (st->b > LLONG_MAX / 8 / std::max(pr.B, 1) || st->h > LLONG_MAX / 8 / std::max(pr.H, 1) ||
       st->r > LLONG_MAX / 8 / std::max(pr.nq, 1))
     return fail(FA_ERR_INVALID_ARGUMENT, "bias strides overflow");
+  // the kernels index a bias row with a 32-bit row stride
+  if (st->r > INT_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "bias row stride %lld exceeds 2^31 - 1 floats", st->r);
   const long long span =
       ((long long)(pr.B - 1) * st->b + (long long)(pr.H - 1) * st->h + (long long)(pr.nq - 1) * st->r + nk) * 4;
   ext->lo = reinterpret_cast<uintptr_t>(bias);

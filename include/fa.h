@@ -180,7 +180,8 @@ int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
  *           bias + b*s0 + h*s1 + i*s2 + j for bias_strides {s0, s1, s2}
  *           (NULL = contiguous [B, H, Nq, Nk]); strides >= 0 (0 broadcasts,
  *           e.g. {0, 0, 0} for one key-padding row shared by all), multiples
- *           of 4 floats, base 16-byte aligned. Entries must be finite or -inf
+ *           of 4 floats, the row stride s2 below 2^31 floats
+ *           (FA_ERR_UNSUPPORTED otherwise), base 16-byte aligned. Entries must be finite or -inf
  *           (-inf removes that key for that query: an arbitrary mask). It is
  *           applied before the band mask and is an input only. 16-bit dtypes
  *           only (FA_FP32 with a bias -> FA_ERR_UNSUPPORTED).

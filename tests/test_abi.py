@@ -219,6 +219,8 @@ def bwd_ex(*, ptrs=None, B=1, H=2, Nq=128, Nk=256, d=64, strides=None, bias=None
     (dict(bias=P[10], Nk=255), fa.FA_ERR_UNSUPPORTED, "multiples of 4 floats"),
     (dict(bias=P[10], dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED, "bf16 and fp16 only"),
     (dict(bias=P[10], o=P[10] + 256), fa.FA_ERR_INVALID_ARGUMENT, "O overlaps bias"),
+    # a row stride the kernels' 32-bit bias index cannot hold (2^31 floats)
+    (dict(bias=P[10], bs=_ll(0, 0, 1 << 31)), fa.FA_ERR_UNSUPPORTED, "exceeds 2^31 - 1"),
 ])
 def test_fwd_ex_rejects_on_the_host(kw, status, needle):
     assert fwd_ex(**kw) == status
@@ -248,6 +250,7 @@ def test_fwd_ex_inputs_may_share_memory():
     (dict(strides=[None] * 4 + [_ll(2 * 128 * 64, 128 * 64, 40)] + [None] * 3), fa.FA_ERR_UNSUPPORTED, "below d"),
     (dict(bias=P[10], ptrs=P[:8] + [P[10] + 64]), fa.FA_ERR_INVALID_ARGUMENT, "dV overlaps the bias"),
     (dict(bias=P[10], bs=_ll(0, 0, 2)), fa.FA_ERR_UNSUPPORTED, "multiples of 4 floats"),
+    (dict(bias=P[10], bs=_ll(0, 0, (1 << 31) + 4)), fa.FA_ERR_UNSUPPORTED, "exceeds 2^31 - 1"),
 ])
 def test_bwd_ex_rejects_on_the_host(kw, status, needle):
     assert bwd_ex(**kw) == status
