@@ -386,6 +386,408 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
       }
 }
 
+// ------------------------------------------- dK, dV split by output ---
+//
+// The kernel above runs one wave per SIMD (its K/V rows, dK/dV accumulators
+// and score tiles take ~340 registers), so its three parts per tile (the S/dP
+// products, the vector work forming P and dS, the dV/dK products) run one
+// after another and the matrix cores idle through the vector work. This one
+// splits the work by output between two waves that share a SIMD, each under
+// 256 registers:
+//  * group A (waves 0-3) owns dV: it forms S = Q K^T and P = exp2(c S - L),
+//    and accumulates dV += P^T dO;
+//  * group B (waves 4-7) owns dK: it forms dP = dO V^T and, with A's P handed
+//    over through LDS, dS = P (dP - D), and accumulates dK += dS^T Q.
+// Waves w and w + 4 own the same 32 keys and run on SIMD w. Their phases
+// alternate, so on each SIMD one wave feeds the matrix core while the other
+// does vector work; each matrix phase is 2 D / 8 MFMAs:
+//   phase 1 of step j:  A: dV += P_{j-1}^T dO_{j-1}, S_j = Q_j K^T | B: dS_{j-1}
+//   phase 2 of step j:  A: P_j (registers, and fp32 into LDS for B)  | B: dK += dS_{j-1}^T Q_{j-1}, dP_j = dO_j V^T
+// Every product and rounding is the one the kernel above performs, in the
+// same order per accumulator, so the two give bit-identical dK and dV.
+// Tile j (Q, dO, statistics) is read from phase 1 of step j to phase 2 of
+// step j + 1, so tiles are triple-buffered; tile j + 1 goes into the slot
+// tile j - 2 left. Both copies are issued outside B's matrix phase: the
+// compiler makes LDS reads wait for direct-to-LDS copies it cannot prove
+// disjoint, and a copy in flight across B's matrix phase stalled its MFMAs.
+//  * A copies Q_{j+1} and its row statistics at the start of its matrix
+//    phase of step j and waits for them at the end of step j (A reads them
+//    in step j + 1, B's dS and dK one phase later).
+//  * B copies dO_{j+1} at the start of its vector phase of step j and waits
+//    for it at the end of phase 1 of step j + 1, before its matrix phase
+//    reads it; the copy of dO_{j+2}, issued in that phase, stays in flight.
+
+constexpr int kPpThreads = 512;
+constexpr int kPpPairs = 4;  // wave pairs (32 keys each) per work-group
+
+struct PpBufs {
+  bf16_t* q;
+  bf16_t* d;
+  float* st;
+};
+
+template <int D>
+struct PpCopy {
+  typedef TileDma<kTile, D, kPpThreads / 2> Dma;  // one group's four waves copy one 64-row tile
+  // vector-memory instructions per wave in one dO copy
+  static constexpr int kBatch = Dma::kInstr;
+  Dma dma;
+  __amdgpu_buffer_rsrc_t qrs, drs, srs;
+  uint32_t q_stride, d_stride;
+  int gwave, lane;
+  // Q and the statistics of a tile (group A)
+  __device__ __forceinline__ void issue_q(const PpBufs& b, int q0) const {
+    dma.issue(qrs, b.q, q0, q_stride);
+    if (gwave == 0 && lane < kStatTileBytes / 16) {
+      FA_LDS void* dst = (FA_LDS void*)(FA_LDS float*)b.st;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, dst, 16, (uint32_t)(q0 / kTile) * kStatTileBytes + 16 * lane,
+                                               0, 0, 0);
+    }
+  }
+  // dO of a tile (group B)
+  __device__ __forceinline__ void issue_d(const PpBufs& b, int q0) const { dma.issue(drs, b.d, q0, d_stride); }
+};
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt bound out of range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Registers of one wave: its 32 keys' K rows (A) or V rows (B) as B
+// operands, its dV (A) or dK (B) accumulators, S (A) or dP (B) of a 64-row
+// tile, and P (A) or dS (B) of the previous tile as bf16 A operands.
+template <int D>
+struct PpState {
+  bf16x8 kv[D / 16];
+  f32x16 acc[D / 32];
+  f32x16 sd[2];
+  bf16x8 pd[4];
+};
+
+// acc += pd^T T with T read transposed from tile `tt` (rows = queries), then
+// sd = R kv^T with R read by rows from tile `rt`. `prev` and `cur` say
+// whether the wave's keys see the previous and the current tile.
+// Scheduling groups (see __builtin_amdgcn_sched_group_barrier): instruction
+// classes the compiler's scheduler must place in the given order. Each block
+// of products keeps kPpAhead LDS operands in flight ahead of its MFMAs;
+// unconstrained, the scheduler issues every read of the block first and runs
+// out of registers.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kPpAhead = 4;
+
+template <typename E, int D>
+__device__ __forceinline__ void pp_matrix(PpState<D>& s, const bf16_t* tt, const bf16_t* rt, bool prev, bool cur,
+                                          const RowRead<D>& rrd, const TrRead<D>& trd) {
+  constexpr int kN = D / 8;  // MFMAs per block: 4 x D / 32 transposed, 2 x D / 16 by rows
+  if (prev) {
+    const FA_LDS char* tb = (const FA_LDS char*)(const FA_LDS bf16_t*)tt;
+    // output blocks interleaved: no MFMA waits on the one just before it
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) s.acc[db] = E::mfma(s.pd[t], trd.at(tb, t, db), s.acc[db]);
+    // two transposed reads per MFMA
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPpAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kN - kPpAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+  if (cur) {
+    const FA_LDS char* rb = (const FA_LDS char*)(const FA_LDS bf16_t*)rt;
+    f32x16 sd[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sd[qb] = E::mfma(rrd.at(rb, qb, ks), s.kv[ks], sd[qb]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s.sd[qb] = sd[qb];
+      fence_regs(s.sd[qb]);
+    }
+    // one row read per MFMA
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPpAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kN - kPpAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+}
+
+// Group A's vector phase: P of the tile in s.sd (scores S of query rows q0 ..
+// q0 + 63 against this lane's key), as bf16 A operands and, in fp32, into the
+// pair's LDS slot for group B. With a band, `masked` tiles set P = 0 where
+// the query row is outside this lane's [q_lo, q_hi].
+template <typename E, int MASK>
+__device__ __forceinline__ void pp_probs(bf16x8 (&pd)[4], const f32x16 (&sd)[2], const float* st, f32x4* pslot,
+                                         float c, int q0, int q_lo, int q_hi, int lane, bool masked) {
+  const int hw = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = qb * 32 + 8 * g + 4 * hw;
+      const f32x4 Lv = *(const FA_LDS f32x4*)((const FA_LDS float*)st + r0);
+      f32x4 pv;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float arg = fmaf(sd[qb][4 * g + rr], c, -Lv[rr]);
+        if (MASK != kMaskNone && masked) {
+          const int qr = q0 + r0 + rr;
+          arg = (qr < q_lo || (MASK == kMaskBand && qr > q_hi)) ? -INFINITY : arg;
+        }
+        pv[rr] = fast_exp2(arg);
+      }
+      *(FA_LDS f32x4*)((FA_LDS f32x4*)pslot + (qb * 4 + g) * 64 + lane) = pv;
+      const int t = qb * 2 + (g >> 1);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pd[t][4 * (g & 1) + rr] = E::cvt(pv[rr]);
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fence_regs(pd[t]);
+}
+
+// Group B's vector phase: dS = P (dP - D) of the previous tile, from group
+// A's P in the pair's LDS slot and this wave's dP in s.sd.
+template <typename E>
+__device__ __forceinline__ void pp_dscores(bf16x8 (&pd)[4], const f32x16 (&sd)[2], const float* st,
+                                           const f32x4* pslot, int lane) {
+  const int hw = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = qb * 32 + 8 * g + 4 * hw;
+      const f32x4 Dv = *(const FA_LDS f32x4*)((const FA_LDS float*)st + kTile + r0);
+      const f32x4 pv = *(const FA_LDS f32x4*)((const FA_LDS f32x4*)pslot + (qb * 4 + g) * 64 + lane);
+      const int t = qb * 2 + (g >> 1);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pd[t][4 * (g & 1) + rr] = E::cvt(pv[rr] * (sd[qb][4 * g + rr] - Dv[rr]));
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fence_regs(pd[t]);
+}
+
+// Whether the wave's keys wk0 .. wk0 + 31 see query tile q0 .. q0 + 63
+// (`live`), and whether some of its pairs are outside the band (`masked`).
+template <int MASK>
+__device__ __forceinline__ void pp_tile_flags(const BwdParams& p, int q0, int wk0, bool& live, bool& masked) {
+  live = wk0 < p.nk;
+  masked = false;
+  if (MASK != kMaskNone) {
+    live = live && q0 + kTile - 1 + p.diag >= wk0 - p.wr;
+    masked = q0 + p.diag < wk0 + 31 - p.wr;
+    if (MASK == kMaskBand) {
+      live = live && q0 + p.diag <= wk0 + 31 + p.wl;
+      masked = masked || q0 + kTile - 1 + p.diag > wk0 + p.wl;
+    }
+  }
+}
+
+// Step j of the loop: tile j in `cur`, tile j - 1 in `prv`, tile j + 1 to
+// be copied into `nxt`. FIRST: there is no tile j - 1. LAST: j = t_end, there
+// is no tile j (only the previous tile's dV, dS and dK remain).
+template <typename E, int D, int MASK, bool GROUP_A, bool FIRST, bool LAST>
+__device__ __forceinline__ void pp_step(int j, int t_end, const PpBufs& cur, const PpBufs& prv, const PpBufs& nxt,
+                                        PpState<D>& s, bool& prev_live, const PpCopy<D>& cp, const RowRead<D>& rrd,
+                                        const TrRead<D>& trd, f32x4* pslot, const BwdParams& p, int wk0, int q_lo,
+                                        int q_hi, int lane) {
+  const int q0 = j * kTile;
+  bool live = false, masked = false;
+  if (!LAST) pp_tile_flags<MASK>(p, q0, wk0, live, masked);
+  const bool prev = !FIRST && prev_live;
+  // phase 1: A's matrix phase, B's vector phase
+  if constexpr (GROUP_A) {
+    if (!LAST && j + 1 < t_end) cp.issue_q(nxt, q0 + kTile);
+    pp_matrix<E, D>(s, prv.d, cur.q, prev, live, rrd, trd);
+  } else {
+    // dO of tile j + 1 into the slot tile j - 2 left
+    if (!LAST && j + 1 < t_end) cp.issue_d(nxt, q0 + kTile);
+    if (prev) pp_dscores<E>(s.pd, s.sd, prv.st, pslot, lane);
+    // tile j's dO, which B reads in the next phase; the copy of tile j + 1
+    // may stay in flight
+    if (!LAST) {
+      if (j + 1 < t_end)
+        wait_vmcnt<PpCopy<D>::kBatch>();
+      else
+        wait_vmem();
+    }
+  }
+  lds_barrier();
+  // phase 2: A's vector phase, B's matrix phase
+  if constexpr (GROUP_A) {
+    if (live) pp_probs<E, MASK>(s.pd, s.sd, cur.st, pslot, p.c, q0, q_lo, q_hi, lane, masked);
+    wait_vmem();  // A's copy of Q_{j+1}
+  } else {
+    pp_matrix<E, D>(s, prv.q, cur.d, prev, live, rrd, trd);
+  }
+  if (!LAST) lds_barrier();
+  prev_live = live;
+}
+
+// The whole loop of one group: tile j sits in buffer (j - t_begin) % 3, and
+// the loop body is unrolled three times so that each copy of the step names
+// fixed buffers.
+template <typename E, int D, int MASK, bool GROUP_A>
+__device__ __forceinline__ void pp_run(int t_begin, int t_end, const PpBufs& b0, const PpBufs& b1, const PpBufs& b2,
+                                       PpState<D>& s, const PpCopy<D>& cp, const RowRead<D>& rrd,
+                                       const TrRead<D>& trd, f32x4* pslot, const BwdParams& p, int wk0, int q_lo,
+                                       int q_hi, int lane) {
+  if (t_begin >= t_end) return;
+  bool prev_live = false;
+  pp_step<E, D, MASK, GROUP_A, true, false>(t_begin, t_end, b0, b2, b1, s, prev_live, cp, rrd, trd, pslot, p, wk0,
+                                            q_lo, q_hi, lane);
+  int j = t_begin + 1;
+  for (; j + 2 < t_end; j += 3) {
+    pp_step<E, D, MASK, GROUP_A, false, false>(j, t_end, b1, b0, b2, s, prev_live, cp, rrd, trd, pslot, p, wk0, q_lo,
+                                               q_hi, lane);
+    pp_step<E, D, MASK, GROUP_A, false, false>(j + 1, t_end, b2, b1, b0, s, prev_live, cp, rrd, trd, pslot, p, wk0,
+                                               q_lo, q_hi, lane);
+    pp_step<E, D, MASK, GROUP_A, false, false>(j + 2, t_end, b0, b2, b1, s, prev_live, cp, rrd, trd, pslot, p, wk0,
+                                               q_lo, q_hi, lane);
+  }
+  if (j < t_end) {
+    pp_step<E, D, MASK, GROUP_A, false, false>(j, t_end, b1, b0, b2, s, prev_live, cp, rrd, trd, pslot, p, wk0, q_lo,
+                                               q_hi, lane);
+    ++j;
+  }
+  if (j < t_end) {
+    pp_step<E, D, MASK, GROUP_A, false, false>(j, t_end, b2, b1, b0, s, prev_live, cp, rrd, trd, pslot, p, wk0, q_lo,
+                                               q_hi, lane);
+    ++j;
+  }
+  // j = t_end: the last tile's dV, dS and dK; that tile sits in buffer (j - 1 - t_begin) % 3
+  const int last = (j - 1 - t_begin) % 3;
+  const PpBufs& lb = last == 0 ? b0 : last == 1 ? b1 : b2;
+  pp_step<E, D, MASK, GROUP_A, false, true>(j, t_end, b0, lb, b0, s, prev_live, cp, rrd, trd, pslot, p, wk0, q_lo,
+                                            q_hi, lane);
+}
+
+template <typename E, int D, int MASK>
+__global__ __launch_bounds__(kPpThreads, 1) void dkdv_pp_kernel(BwdParams p) {
+  constexpr int P = lds_pitch<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds2[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t d_lds2[kTile * P];
+  __shared__ __attribute__((aligned(16))) float s_lds0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) float s_lds1[2 * kTile];
+  __shared__ __attribute__((aligned(16))) float s_lds2[2 * kTile];
+  // P of each wave pair's 64 x 32 tile, fp32, one 16-byte chunk per lane per
+  // (query block, group of 4 rows)
+  __shared__ __attribute__((aligned(1024))) f32x4 p_lds[kPpPairs * 8 * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_a = wave < kPpPairs;
+  const int pair = wave & (kPpPairs - 1);
+  const int hw = lane >> 5;
+  const int col = lane & 31;
+  const int nq = p.nq, nk = p.nk;
+
+  const int logical = xcd_logical_block(blockIdx.x, (int)gridDim.x);
+  const int head = logical / p.nkb;
+  const int kblk = logical - head * p.nkb;
+  const int key_wg = kblk * kRowsPerBlock;
+  const int wk0 = key_wg + pair * kRowsPerWave;
+  const int key = wk0 + col;
+  // query rows that see this lane's key: [key - diag - wr, key - diag + wl]
+  const int q_lo = key - p.diag - p.wr, q_hi = key - p.diag + p.wl;
+
+  // query tiles of this work-group's band
+  int t_begin = 0, t_end = (nq + kTile - 1) / kTile;
+  if (MASK != kMaskNone) {
+    const int r_lo = max(0, key_wg - p.diag - p.wr);
+    const int r_hi = min(nq - 1, key_wg + kRowsPerBlock - 1 - p.diag + p.wl);
+    t_begin = r_lo / kTile;
+    t_end = r_hi < r_lo ? t_begin : r_hi / kTile + 1;
+  }
+
+  const bf16_t* qh = head_base(p.q, p.q_sb, p.q_sh, p.heads, head);
+  const bf16_t* dh = head_base(p.dout, p.do_sb, p.do_sh, p.heads, head);
+  PpCopy<D> cp;
+  cp.dma.init(pair, lane);
+  cp.qrs = rows_rsrc<D>(qh, nq, 2u * p.q_sr);
+  cp.drs = rows_rsrc<D>(dh, nq, 2u * p.do_sr);
+  cp.srs = make_rsrc(p.stats + (long long)head * p.nq_pad * 2, (uint32_t)p.nq_pad * 8);
+  cp.q_stride = 2u * p.q_sr;
+  cp.d_stride = 2u * p.do_sr;
+  cp.gwave = pair;
+  cp.lane = lane;
+  const PpBufs b0{q_lds0, d_lds0, s_lds0}, b1{q_lds1, d_lds1, s_lds1}, b2{q_lds2, d_lds2, s_lds2};
+  // tile t_begin: A copies Q and the statistics, B copies dO
+  if (t_begin < t_end) {
+    if (group_a) {
+      cp.issue_q(b0, t_begin * kTile);
+    } else {
+      cp.issue_d(b0, t_begin * kTile);
+    }
+  }
+
+  // A: the K rows of its keys; B: the V rows
+  PpState<D> s;
+  {
+    const bf16_t* src = group_a ? head_base(p.k, p.k_sb, p.k_sh, p.heads, head)
+                                : head_base(p.v, p.v_sb, p.v_sh, p.heads, head);
+    const long long sr = group_a ? p.k_sr : p.v_sr;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (key < nk) x = *(const u32x4*)(src + (long long)key * sr + 16 * ks + 8 * hw);
+      s.kv[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) s.acc[db] = f32x16{};
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) s.sd[qb] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s.pd[t] = bf16x8{};
+  RowRead<D> rrd;
+  rrd.init(lane);
+  TrRead<D> trd;
+  trd.init(lane);
+  f32x4* pslot = p_lds + pair * 8 * 64;
+
+  // K / V rows and tile t_begin
+  wait_vmem();
+  lds_barrier();
+  // The two groups run separate copies of the loop (the same sequence of
+  // work-group barriers): one loop holding both groups' values at every
+  // phase join needs more registers than two waves per SIMD leave.
+  if (group_a)
+    pp_run<E, D, MASK, true>(t_begin, t_end, b0, b1, b2, s, cp, rrd, trd, pslot, p, wk0, q_lo, q_hi, lane);
+  else
+    pp_run<E, D, MASK, false>(t_begin, t_end, b0, b1, b2, s, cp, rrd, trd, pslot, p, wk0, q_lo, q_hi, lane);
+
+  // lane holds d = 32 db + col for keys wk0 + 8 g + 4 hw + rr; A stores dV, B stores dK (x scale)
+  bf16_t* outh = group_a ? (bf16_t*)head_base(p.dv, p.dv_sb, p.dv_sh, p.heads, head)
+                         : (bf16_t*)head_base(p.dk, p.dk_sb, p.dk_sh, p.heads, head);
+  const long long osr = group_a ? p.dv_sr : p.dk_sr;
+  const float oscale = group_a ? 1.f : p.scale;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int kr = wk0 + 8 * g + 4 * hw + rr;
+        if (kr < nk) outh[(long long)kr * osr + 32 * db + col] = __builtin_bit_cast(bf16_t, E::cvt(s.acc[db][4 * g + rr] * oscale));
+      }
+}
+
 // -------------------------------------------------------------------- dQ ---
 
 // One 64-key tile against the wave's 32 query rows. `masked` tiles set P = 0
@@ -610,6 +1012,10 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   template __global__ void dq_kernel<E, D, kMaskNone, B>(BwdParams);    \
   template __global__ void dq_kernel<E, D, kMaskUpper, B>(BwdParams);   \
   template __global__ void dq_kernel<E, D, kMaskBand, B>(BwdParams);
+#define FA_BWD_PP_INSTANCES(E, D)                                 \
+  template __global__ void dkdv_pp_kernel<E, D, kMaskNone>(BwdParams);  \
+  template __global__ void dkdv_pp_kernel<E, D, kMaskUpper>(BwdParams); \
+  template __global__ void dkdv_pp_kernel<E, D, kMaskBand>(BwdParams);
 #define FA_BWD_INSTANCES(E, D)                                                                             \
   FA_BWD_INSTANCES_B(E, D, false)                                                                         \
   FA_BWD_INSTANCES_B(E, D, true)                                                                          \
@@ -623,6 +1029,15 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   FA_BWD_INSTANCES(E, 256)
 FA_BWD_INSTANCES_D(Bf16)
 FA_BWD_INSTANCES_D(F16)
+#define FA_BWD_PP_INSTANCES_D(E) \
+  FA_BWD_PP_INSTANCES(E, 32)     \
+  FA_BWD_PP_INSTANCES(E, 64)     \
+  FA_BWD_PP_INSTANCES(E, 96)     \
+  FA_BWD_PP_INSTANCES(E, 128)
+FA_BWD_PP_INSTANCES_D(Bf16)
+FA_BWD_PP_INSTANCES_D(F16)
+#undef FA_BWD_PP_INSTANCES_D
+#undef FA_BWD_PP_INSTANCES
 #undef FA_BWD_INSTANCES_D
 #undef FA_BWD_INSTANCES
 #undef FA_BWD_INSTANCES_B
@@ -674,7 +1089,14 @@ hipError_t launch(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (p.nkb > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<E, D, MASK, BIAS>), dim3((unsigned)(p.nkb * bh)), dim3(kThreads), 0, a.stream, p);
+    // without a bias and for d <= 128 (whose triple-buffered tiles fit the
+    // LDS), the kernel split by output between two waves per SIMD
+    if constexpr (!BIAS && D <= 128)
+      hipLaunchKernelGGL((dkdv_pp_kernel<E, D, MASK>), dim3((unsigned)(p.nkb * bh)), dim3(kPpThreads), 0, a.stream,
+                         p);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<E, D, MASK, BIAS>), dim3((unsigned)(p.nkb * bh)), dim3(kThreads), 0, a.stream,
+                         p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

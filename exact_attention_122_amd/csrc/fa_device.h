@@ -173,6 +173,10 @@ struct RowRead {
     return *(const FA_LDS bf16x8*)((const FA_LDS char*)(const FA_LDS bf16_t*)tile + off[ks % kOff] +
                                    (ks / kOff) * 256 + kb * 32 * P * 2);
   }
+  // the same read from a tile given by its LDS byte address
+  __device__ __forceinline__ bf16x8 at(const FA_LDS char* base, int kb, int ks) const {
+    return *(const FA_LDS bf16x8*)(base + off[ks % kOff] + (ks / kOff) * 256 + kb * 32 * P * 2);
+  }
 };
 
 template <int D>
@@ -200,7 +204,17 @@ struct TrRead {
     i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8, z);
   }
+  // the same read from a tile given by its LDS byte address
+  __device__ __forceinline__ bf16x8 at(const FA_LDS char* base, int t, int db) const {
+    const FA_LDS char* b = base + t * 16 * P * 2 + (db / kOff) * 256;
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + off[db % kOff][0]));
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + off[db % kOff][1]));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(bf16x8, z);
+  }
 };
+
 
 // Direct global -> LDS tile copy (buffer_load ... lds, 16 bytes per lane).
 // A ROWS x D tile of 16-bit elements is THREADS/64 waves x kInstr

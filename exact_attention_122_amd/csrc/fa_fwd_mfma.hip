@@ -185,6 +185,27 @@ __device__ __forceinline__ f32x4 load_bias4(const float* brow, int kc, int nk) {
   return bv;
 }
 
+// Maximum of N values as a tree of three-input maxima (v_max3_f32): each
+// level turns groups of three into one, so the tree takes about N / 2
+// instructions instead of N - 1, with independent instructions side by side.
+template <int N>
+__device__ __forceinline__ float max_tree(const float* x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return fmaxf(x[0], x[1]);
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float t[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int a = 3 * i;
+      t[i] = a + 2 < N ? fmaxf(fmaxf(x[a], x[a + 1]), x[a + 2]) : a + 1 < N ? fmaxf(x[a], x[a + 1]) : x[a];
+    }
+    return max_tree<M>(t);
+  }
+}
+
 // Softmax phase for the tile whose scores are in st.s. With a bias the scores
 // become y = c s + log2(e) bias (log2 units) first; `masked` tiles (band
 // edges, ragged end) then set the scores of dead keys to -inf.
@@ -233,18 +254,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
   // Running max: in-lane as a tree, then across the half-wave pair. The
   // softmax wave has its SIMD's vector ALU to itself during this phase, so
   // only independent instructions hide each other's latency.
-  float mx;
-  {
-    float t[kN / 2];
-#pragma unroll
-    for (int i = 0; i < kN / 2; ++i) t[i] = fmaxf(x[i], x[i + kN / 2]);
-#pragma unroll
-    for (int w = kN / 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-    mx = t[0];
-  }
-  mx = pair_max(mx);
+  const float mx = pair_max(max_tree<kN>(x));
 
   if (wave_any(!(mx <= st.m + thr))) {
     const float mnew = fmaxf(st.m, mx);

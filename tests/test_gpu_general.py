@@ -378,3 +378,26 @@ def test_zero_bias_matches_no_bias():
     torch.cuda.synchronize()
     assert float((o0.float() - o1.float()).abs().max()) < 1e-2
     assert float((l0 - l1).abs().max()) < 1e-4
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("nq,nk,window", [(333, 333, (-1, 0)), (517, 517, (-1, -1)), (200, 1100, (-1, 0)),
+                                          (700, 700, (100, 20)), (64, 64, (-1, -1))])
+def test_bwd_split_dkdv_kernel_equals_single_role_kernel_bitwise(d, dtype, nq, nk, window):
+    """Without a bias and for d <= 128, dK and dV come from the kernel that
+    splits the work by output between two waves per SIMD (one forms P and dV,
+    the other dP, dS and dK); with a bias, from the kernel in which one wave
+    does all of it. A zero bias adds log2(e) * 0 to every exponent, so both
+    run the same products and roundings in the same order per accumulator:
+    given the same O and LSE, all three gradients must agree bit for bit."""
+    g = inputs.generate(1, 2, nq, d, dtype, seed=8500 + d + nq, with_grad_output=True, nk=nk)
+    q, k, v, do = (to_dev(g[x]) for x in ("q", "k", "v", "do"))
+    scale = inputs.default_scale(d)
+    o, lse = fa.fa_fwd_ex(q, k, v, window=window, scale=scale)
+    zero = torch.zeros(1, 1, 1, nk, dtype=torch.float32, device="cuda")
+    split = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale)
+    single = fa.fa_bwd_ex(q, k, v, o, do, lse, window=window, scale=scale, bias=zero)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), split, single):
+        assert torch.equal(a, b), f"{name} differs between the two dK/dV kernels"
