@@ -887,7 +887,9 @@ constexpr int dq_blocks_per_cu() {
   return D >= 256 ? 1 : 2;
 }
 
-template <typename E, int D, int MASK, bool BIAS>
+// RAGGED (kernels without a band only): N_k is not a multiple of the 64-key
+// tile, so the last tile must mask keys past the end.
+template <typename E, int D, int MASK, bool BIAS, bool RAGGED>
 __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(BwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
   constexpr int P = lds_pitch<D>();
@@ -970,25 +972,19 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
 
   wait_vmem();
   __syncthreads();
-  // Without a band only a ragged last tile needs masking (a zero K row past
-  // the end would get p = exp2(-LSE log2 e), which overflows for very
-  // negative LSE): it runs after the main loop, in a copy of the step that
-  // has the masking code.
-  const int n_main = BAND ? n_tiles : min(n_tiles, nk / kTile);
-  for (int j = 0; j < n_main; j += 2) {
-    dq_step<E, D, MASK, BIAS, BAND>(j, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf, df,
-                              dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
-    if (j + 1 < n_main)
-      dq_step<E, D, MASK, BIAS, BAND>(j + 1, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
-  }
-  if (!BAND && n_main < n_tiles) {
-    if (n_main & 1)
-      dq_step<E, D, MASK, BIAS, true>(n_main, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
-    else
-      dq_step<E, D, MASK, BIAS, true>(n_main, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd, qf,
-                                df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
+  // Tiles carry masking code only where some can need it: with a band, or
+  // when the last key tile is ragged (a zero K row past the end would get
+  // p = exp2(-LSE log2 e), which overflows for very negative LSE). Without
+  // either, the loop has no branch in the middle of its tiles. (A separate
+  // masked copy of the step for the ragged tile alone, after the main loop,
+  // cost the kernel 12 spilled registers at d = 128.)
+  constexpr bool MASK_CODE = BAND || RAGGED;
+  for (int j = 0; j < n_tiles; j += 2) {
+    dq_step<E, D, MASK, BIAS, MASK_CODE>(j, n_tiles, key_base, k_lds0, v_lds0, k_lds1, v_lds1, dma, krs, vrs, rrd, trd,
+                                         qf, df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
+    if (j + 1 < n_tiles)
+      dq_step<E, D, MASK, BIAS, MASK_CODE>(j + 1, n_tiles, key_base, k_lds1, v_lds1, k_lds0, v_lds0, dma, krs, vrs, rrd,
+                                           trd, qf, df, dq, lse2, drow, p, k_lo, k_hi, wq0, lane, brow);
   }
 
   if (qi < nq) {
@@ -1005,42 +1001,42 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   }
 }
 
-#define FA_BWD_INSTANCES_B(E, D, B)                                     \
-  template __global__ void dkdv_kernel<E, D, kMaskNone, B>(BwdParams);  \
-  template __global__ void dkdv_kernel<E, D, kMaskUpper, B>(BwdParams); \
-  template __global__ void dkdv_kernel<E, D, kMaskBand, B>(BwdParams);  \
-  template __global__ void dq_kernel<E, D, kMaskNone, B>(BwdParams);    \
-  template __global__ void dq_kernel<E, D, kMaskUpper, B>(BwdParams);   \
-  template __global__ void dq_kernel<E, D, kMaskBand, B>(BwdParams);
-#define FA_BWD_PP_INSTANCES(E, D)                                 \
+// The kernels the launchers below can reach: the single-role dK/dV kernel
+// with a bias, and without one at d = 256; the split dK/dV kernel for d <= 128
+// without a bias; dQ (the ragged variant only without a band).
+#define FA_BWD_DQ(E, D, B)                                                    \
+  template __global__ void dq_kernel<E, D, kMaskNone, B, false>(BwdParams);  \
+  template __global__ void dq_kernel<E, D, kMaskNone, B, true>(BwdParams);   \
+  template __global__ void dq_kernel<E, D, kMaskUpper, B, false>(BwdParams); \
+  template __global__ void dq_kernel<E, D, kMaskBand, B, false>(BwdParams);
+#define FA_BWD_COMMON(E, D)                                                                                      \
+  template __global__ void dkdv_kernel<E, D, kMaskNone, true>(BwdParams);                                     \
+  template __global__ void dkdv_kernel<E, D, kMaskUpper, true>(BwdParams);                                    \
+  template __global__ void dkdv_kernel<E, D, kMaskBand, true>(BwdParams);                                     \
+  FA_BWD_DQ(E, D, false)                                                                                         \
+  FA_BWD_DQ(E, D, true)                                                                                          \
+  template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
+                                                  Strides, int, int, int, long long);
+#define FA_BWD_SPLIT(E, D)                                                \
+  FA_BWD_COMMON(E, D)                                                     \
   template __global__ void dkdv_pp_kernel<E, D, kMaskNone>(BwdParams);  \
   template __global__ void dkdv_pp_kernel<E, D, kMaskUpper>(BwdParams); \
   template __global__ void dkdv_pp_kernel<E, D, kMaskBand>(BwdParams);
-#define FA_BWD_INSTANCES(E, D)                                                                             \
-  FA_BWD_INSTANCES_B(E, D, false)                                                                         \
-  FA_BWD_INSTANCES_B(E, D, true)                                                                          \
-  template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
-                                                  Strides, int, int, int, long long);
-#define FA_BWD_INSTANCES_D(E) \
-  FA_BWD_INSTANCES(E, 32)     \
-  FA_BWD_INSTANCES(E, 64)     \
-  FA_BWD_INSTANCES(E, 96)     \
-  FA_BWD_INSTANCES(E, 128)    \
-  FA_BWD_INSTANCES(E, 256)
-FA_BWD_INSTANCES_D(Bf16)
-FA_BWD_INSTANCES_D(F16)
-#define FA_BWD_PP_INSTANCES_D(E) \
-  FA_BWD_PP_INSTANCES(E, 32)     \
-  FA_BWD_PP_INSTANCES(E, 64)     \
-  FA_BWD_PP_INSTANCES(E, 96)     \
-  FA_BWD_PP_INSTANCES(E, 128)
-FA_BWD_PP_INSTANCES_D(Bf16)
-FA_BWD_PP_INSTANCES_D(F16)
-#undef FA_BWD_PP_INSTANCES_D
-#undef FA_BWD_PP_INSTANCES
-#undef FA_BWD_INSTANCES_D
-#undef FA_BWD_INSTANCES
-#undef FA_BWD_INSTANCES_B
+#define FA_BWD_ALL(E)                                                     \
+  FA_BWD_SPLIT(E, 32)                                                     \
+  FA_BWD_SPLIT(E, 64)                                                     \
+  FA_BWD_SPLIT(E, 96)                                                     \
+  FA_BWD_SPLIT(E, 128)                                                    \
+  FA_BWD_COMMON(E, 256)                                                   \
+  template __global__ void dkdv_kernel<E, 256, kMaskNone, false>(BwdParams);  \
+  template __global__ void dkdv_kernel<E, 256, kMaskUpper, false>(BwdParams); \
+  template __global__ void dkdv_kernel<E, 256, kMaskBand, false>(BwdParams);
+FA_BWD_ALL(Bf16)
+FA_BWD_ALL(F16)
+#undef FA_BWD_ALL
+#undef FA_BWD_SPLIT
+#undef FA_BWD_COMMON
+#undef FA_BWD_DQ
 
 template <typename E, int D, int MASK, bool BIAS>
 hipError_t launch(const BwdArgs& a) {
@@ -1101,7 +1097,16 @@ hipError_t launch(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (p.nqb > 0) {
-    hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0, a.stream, p);
+    // without a band, a ragged last key tile needs the masking variant
+    if constexpr (MASK == kMaskNone) {
+      if (g.nk % kTile != 0) {
+        hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, true>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0,
+                           a.stream, p);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, false>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0,
+                       a.stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
