@@ -1001,9 +1001,285 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   }
 }
 
+// ------------------------------------------------ dQ, two wave groups ---
+//
+// The kernel above runs two independent work-groups per CU, so whether one
+// wave's MFMAs overlap the other wave's vector work on a SIMD is left to
+// chance. This one (no bias, d = 96 and 128) runs one work-group of 8 waves (256
+// query rows) per CU as two groups of four with the forward pass's
+// ping-pong: each wave's work per 64-key tile splits into a matrix phase
+// (dQ^T += K_{j-1}^T dS_{j-1}^T for the previous tile, then S^T_j = K_j Q^T
+// and dP^T_j = V_j dO^T) and a vector phase (P and dS of tile j), group B
+// runs one work-group barrier behind group A, and so on every SIMD one wave
+// feeds the matrix core while the other does vector work. Products and
+// roundings are the kernel above's, in the same order per accumulator.
+// K_j is read in matrix phases j and j + 1, so K and V tiles are
+// triple-buffered; group A copies K_{j+1} and V_{j+1} (into the slot of tile
+// j - 2) at the start of its matrix phase j and waits for them at the end of
+// its vector phase j, before their first reader (its matrix phase j + 1).
+// Group B never has a copy in flight.
+
+constexpr int kDqpThreads = 512;
+constexpr int kDqpRows = 256;  // query rows per work-group
+
+struct DqpBufs {
+  bf16_t* k;
+  bf16_t* v;
+};
+
+template <int D>
+struct DqpState {
+  bf16x8 qf[D / 16], df[D / 16];  // this lane's Q and dO rows as B operands
+  f32x16 dq[D / 32];              // dQ^T: register r of dq[db] holds d = 32 db + 8 (r / 4) + 4 hw + r % 4
+  f32x16 s[2], dpt[2];            // S^T and dP^T of the current tile (lane = query)
+  bf16x8 ds[4];                   // dS^T of the previous tile as bf16 B operands
+  float lse2, drow;
+};
+
+template <typename E, int D>
+__device__ __forceinline__ void dqp_matrix(DqpState<D>& st, const bf16_t* kprev, const bf16_t* kcur,
+                                           const bf16_t* vcur, bool prev, bool cur, const RowRead<D>& rrd,
+                                           const TrRead<D>& trd) {
+  constexpr int kN = D / 8;  // transposed dQ MFMAs (4 x D / 32), two reads each
+  if (prev) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) st.dq[db] = E::mfma(trd(kprev, t, db), st.ds[t], st.dq[db]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPpAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kN - kPpAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+  if (cur) {
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = E::mfma(rrd(kcur, kb, ks), st.qf[ks], s[kb]);
+        dp[kb] = E::mfma(rrd(vcur, kb, ks), st.df[ks], dp[kb]);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st.s[kb] = s[kb];
+      st.dpt[kb] = dp[kb];
+      fence_regs(st.s[kb]);
+      fence_regs(st.dpt[kb]);
+    }
+    // one row read per MFMA
+    constexpr int kR = D / 4;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPpAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kR - kPpAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+}
+
+// Vector phase: dS^T = P (dP - D) of the tile in st.s / st.dpt, keys key0 ..
+// key0 + 63. `masked` tiles (band edges, ragged end; MASK_CODE kernels only)
+// set P = 0 for keys outside this lane's [k_lo, k_hi].
+template <typename E, int MASK, bool MASK_CODE>
+__device__ __forceinline__ void dqp_vector(bf16x8 (&ds)[4], const f32x16 (&s)[2], const f32x16 (&dpt)[2], float lse2,
+                                           float drow, float c, int key0, int k_lo, int k_hi, int lane, bool masked) {
+  const int hw = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arg = fmaf(s[kb][i], c, -lse2);
+      if (MASK_CODE && masked) {
+        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hw + (i & 3);
+        arg = (key > k_hi || (MASK == kMaskBand && key < k_lo)) ? -INFINITY : arg;
+      }
+      const float pv = fast_exp2(arg);
+      ds[kb * 2 + (i >> 3)][i & 7] = E::cvt(pv * (dpt[kb][i] - drow));
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fence_regs(ds[t]);
+}
+
+// Whether the wave's query rows wq0 .. wq0 + 31 see key tile key0 .. key0 +
+// 63 (`live`) and whether the tile needs masking (`masked`).
+template <int MASK>
+__device__ __forceinline__ void dqp_tile_flags(const BwdParams& p, int key0, int wq0, bool& live, bool& masked) {
+  live = wq0 < p.nq;
+  masked = key0 + kTile > p.nk;
+  if (MASK != kMaskNone) {
+    live = live && key0 <= wq0 + 31 + p.diag + p.wr;
+    masked = masked || key0 + kTile - 1 > wq0 + p.diag + p.wr;
+    if (MASK == kMaskBand) {
+      live = live && key0 + kTile - 1 >= wq0 + p.diag - p.wl;
+      masked = masked || key0 < wq0 + 31 + p.diag - p.wl;
+    }
+  }
+}
+
+// Iteration j (0 <= j <= n_tiles) of one wave: matrix phase j (tile j - 1 in
+// `prv`, tile j in `cur`), a barrier, vector phase j, a barrier. Group A
+// copies tile j + 1 into `nxt` at the start of its matrix phase.
+template <typename E, int D, int MASK, bool MASK_CODE>
+__device__ __forceinline__ void dqp_iteration(int j, int n_tiles, int key_base, bool group_a, const DqpBufs& cur,
+                                              const DqpBufs& prv, const DqpBufs& nxt,
+                                              const TileDma<kTile, D, kDqpThreads / 2>& dma,
+                                              __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                              const RowRead<D>& rrd, const TrRead<D>& trd, DqpState<D>& st,
+                                              bool& prev_live, const BwdParams& p, int wq0, int k_lo, int k_hi,
+                                              int lane) {
+  const int key0 = key_base + j * kTile;
+  bool live = false, masked = false;
+  if (j < n_tiles) dqp_tile_flags<MASK>(p, key0, wq0, live, masked);
+  if (group_a && j + 1 < n_tiles) {
+    dma.issue(krs, nxt.k, key0 + kTile, 2u * p.k_sr);
+    dma.issue(vrs, nxt.v, key0 + kTile, 2u * p.v_sr);
+  }
+  dqp_matrix<E, D>(st, prv.k, cur.k, cur.v, j > 0 && prev_live, live, rrd, trd);
+  lds_barrier();
+  if (live)
+    dqp_vector<E, MASK, MASK_CODE>(st.ds, st.s, st.dpt, st.lse2, st.drow, p.c, key0, k_lo, k_hi, lane, masked);
+  if (group_a) wait_vmem();  // tile j + 1, read from the next matrix phase on
+  lds_barrier();
+  prev_live = live;
+}
+
+template <typename E, int D, int MASK, bool RAGGED>
+__global__ __launch_bounds__(kDqpThreads, 1) void dq_pp_kernel(BwdParams p) {
+  constexpr bool BAND = MASK != kMaskNone;
+  constexpr bool MASK_CODE = BAND || RAGGED;
+  constexpr int P = lds_pitch<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds2[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[kTile * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds2[kTile * P];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_a = wave < 4;
+  const int hw = lane >> 5;
+  const int col = lane & 31;
+  const int nq = p.nq, nk = p.nk;
+
+  const int logical = xcd_logical_block(blockIdx.x, (int)gridDim.x);
+  const int head = logical / p.nqb;
+  int qblk = logical - head * p.nqb;
+  if (BAND) qblk = p.nqb - 1 - qblk;  // longest rows first under a causal band
+  const int q_row0 = qblk * kDqpRows;
+  const int wq0 = q_row0 + wave * kRowsPerWave;
+  const int qi = wq0 + col;
+  // live keys of this lane's row: [k_lo, k_hi]
+  const int k_lo = BAND ? qi + p.diag - p.wl : 0;
+  const int k_hi = BAND ? min(nk - 1, qi + p.diag + p.wr) : nk - 1;
+
+  // key tiles of this work-group's band
+  const int q_last = min(nq, q_row0 + kDqpRows) - 1;
+  int key_base = 0, n_tiles = (nk + kTile - 1) / kTile;
+  if (BAND) {
+    const int c_lo = max(0, q_row0 + p.diag - p.wl);
+    const int c_hi = min(nk - 1, q_last + p.diag + p.wr);
+    key_base = c_lo / kTile * kTile;
+    n_tiles = c_hi < c_lo ? 0 : (c_hi - key_base) / kTile + 1;
+  }
+
+  const bf16_t* qh = head_base(p.q, p.q_sb, p.q_sh, p.heads, head);
+  const bf16_t* dh = head_base(p.dout, p.do_sb, p.do_sh, p.heads, head);
+  const bf16_t* kh = head_base(p.k, p.k_sb, p.k_sh, p.heads, head);
+  const bf16_t* vh = head_base(p.v, p.v_sb, p.v_sh, p.heads, head);
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc<D>(kh, nk, 2u * p.k_sr);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc<D>(vh, nk, 2u * p.v_sr);
+  TileDma<kTile, D, kDqpThreads / 2> dma;  // group A's four waves copy every tile
+  dma.init(wave & 3, lane);
+  const DqpBufs b0{k_lds0, v_lds0}, b1{k_lds1, v_lds1}, b2{k_lds2, v_lds2};
+  if (group_a && n_tiles > 0) {
+    dma.issue(krs, b0.k, key_base, 2u * p.k_sr);
+    dma.issue(vrs, b0.v, key_base, 2u * p.v_sr);
+  }
+
+  DqpState<D> st;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 qx = u32x4{0u, 0u, 0u, 0u}, dx = qx;
+    if (qi < nq) {
+      qx = *(const u32x4*)(qh + (long long)qi * p.q_sr + 16 * ks + 8 * hw);
+      dx = *(const u32x4*)(dh + (long long)qi * p.do_sr + 16 * ks + 8 * hw);
+    }
+    st.qf[ks] = __builtin_bit_cast(bf16x8, qx);
+    st.df[ks] = __builtin_bit_cast(bf16x8, dx);
+  }
+  st.lse2 = 0.f;
+  st.drow = 0.f;
+  if (qi < nq) {
+    const float* sp = p.stats + ((long long)head * p.nq_pad + (qi & ~(kTile - 1))) * 2;
+    st.lse2 = sp[qi & (kTile - 1)];
+    st.drow = sp[kTile + (qi & (kTile - 1))];
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.dq[db] = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) st.s[kb] = st.dpt[kb] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.ds[t] = bf16x8{};
+  RowRead<D> rrd;
+  rrd.init(lane);
+  TrRead<D> trd;
+  trd.init(lane);
+
+  wait_vmem();
+  lds_barrier();
+  // Group B runs one barrier behind group A: while A is in its matrix phase
+  // j, B is in its vector phase j - 1, and the other way round.
+  if (!group_a) lds_barrier();
+  bool prev_live = false;
+  // tile j sits in slot j % 3; iteration n_tiles only adds the last tile's dQ
+  int j = 0;
+  for (; j + 2 <= n_tiles; j += 3) {
+    dqp_iteration<E, D, MASK, MASK_CODE>(j, n_tiles, key_base, group_a, b0, b2, b1, dma, krs, vrs, rrd, trd, st,
+                                         prev_live, p, wq0, k_lo, k_hi, lane);
+    dqp_iteration<E, D, MASK, MASK_CODE>(j + 1, n_tiles, key_base, group_a, b1, b0, b2, dma, krs, vrs, rrd, trd, st,
+                                         prev_live, p, wq0, k_lo, k_hi, lane);
+    dqp_iteration<E, D, MASK, MASK_CODE>(j + 2, n_tiles, key_base, group_a, b2, b1, b0, dma, krs, vrs, rrd, trd, st,
+                                         prev_live, p, wq0, k_lo, k_hi, lane);
+  }
+  if (j <= n_tiles) {
+    dqp_iteration<E, D, MASK, MASK_CODE>(j, n_tiles, key_base, group_a, b0, b2, b1, dma, krs, vrs, rrd, trd, st,
+                                         prev_live, p, wq0, k_lo, k_hi, lane);
+    ++j;
+  }
+  if (j <= n_tiles) {
+    dqp_iteration<E, D, MASK, MASK_CODE>(j, n_tiles, key_base, group_a, b1, b0, b2, dma, krs, vrs, rrd, trd, st,
+                                         prev_live, p, wq0, k_lo, k_hi, lane);
+  }
+  if (group_a) lds_barrier();
+
+  if (qi < nq) {
+    bf16_t* row = (bf16_t*)head_base(p.dq, p.dq_sb, p.dq_sh, p.heads, head) + (long long)qi * p.dq_sr;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack2<E>(st.dq[db][4 * g] * p.scale, st.dq[db][4 * g + 1] * p.scale);
+        w.y = pack2<E>(st.dq[db][4 * g + 2] * p.scale, st.dq[db][4 * g + 3] * p.scale);
+        *(uint2*)(row + db * 32 + 8 * g + 4 * hw) = w;
+      }
+  }
+}
+
 // The kernels the launchers below can reach: the single-role dK/dV kernel
-// with a bias, and without one at d = 256; the split dK/dV kernel for d <= 128
-// without a bias; dQ (the ragged variant only without a band).
+// and the one-group dQ kernel with a bias, and without one at d = 256; the
+// split dK/dV kernel for d <= 128 without a bias; the two-group dQ kernel for
+// d = 96 and 128 without a bias, the one-group one below (ragged dQ variants
+// only without a band).
 #define FA_BWD_DQ(E, D, B)                                                    \
   template __global__ void dq_kernel<E, D, kMaskNone, B, false>(BwdParams);  \
   template __global__ void dq_kernel<E, D, kMaskNone, B, true>(BwdParams);   \
@@ -1013,21 +1289,30 @@ __global__ __launch_bounds__(kThreads, dq_blocks_per_cu<D>()) void dq_kernel(Bwd
   template __global__ void dkdv_kernel<E, D, kMaskNone, true>(BwdParams);                                     \
   template __global__ void dkdv_kernel<E, D, kMaskUpper, true>(BwdParams);                                    \
   template __global__ void dkdv_kernel<E, D, kMaskBand, true>(BwdParams);                                     \
-  FA_BWD_DQ(E, D, false)                                                                                         \
   FA_BWD_DQ(E, D, true)                                                                                          \
   template __global__ void row_stats_kernel<E, D>(const bf16_t*, const bf16_t*, const float*, float*, Strides, \
                                                   Strides, int, int, int, long long);
-#define FA_BWD_SPLIT(E, D)                                                \
-  FA_BWD_COMMON(E, D)                                                     \
-  template __global__ void dkdv_pp_kernel<E, D, kMaskNone>(BwdParams);  \
-  template __global__ void dkdv_pp_kernel<E, D, kMaskUpper>(BwdParams); \
+#define FA_BWD_SPLIT(E, D)                                                   \
+  FA_BWD_COMMON(E, D)                                                        \
+  template __global__ void dkdv_pp_kernel<E, D, kMaskNone>(BwdParams);       \
+  template __global__ void dkdv_pp_kernel<E, D, kMaskUpper>(BwdParams);      \
   template __global__ void dkdv_pp_kernel<E, D, kMaskBand>(BwdParams);
-#define FA_BWD_ALL(E)                                                     \
-  FA_BWD_SPLIT(E, 32)                                                     \
-  FA_BWD_SPLIT(E, 64)                                                     \
-  FA_BWD_SPLIT(E, 96)                                                     \
-  FA_BWD_SPLIT(E, 128)                                                    \
-  FA_BWD_COMMON(E, 256)                                                   \
+#define FA_BWD_DQPP(E, D)                                                    \
+  template __global__ void dq_pp_kernel<E, D, kMaskNone, false>(BwdParams);  \
+  template __global__ void dq_pp_kernel<E, D, kMaskNone, true>(BwdParams);   \
+  template __global__ void dq_pp_kernel<E, D, kMaskUpper, false>(BwdParams); \
+  template __global__ void dq_pp_kernel<E, D, kMaskBand, false>(BwdParams);
+#define FA_BWD_ALL(E)                                                         \
+  FA_BWD_SPLIT(E, 32)                                                         \
+  FA_BWD_DQ(E, 32, false)                                                     \
+  FA_BWD_SPLIT(E, 64)                                                         \
+  FA_BWD_DQ(E, 64, false)                                                     \
+  FA_BWD_SPLIT(E, 96)                                                         \
+  FA_BWD_DQPP(E, 96)                                                          \
+  FA_BWD_SPLIT(E, 128)                                                        \
+  FA_BWD_DQPP(E, 128)                                                         \
+  FA_BWD_COMMON(E, 256)                                                       \
+  FA_BWD_DQ(E, 256, false)                                                    \
   template __global__ void dkdv_kernel<E, 256, kMaskNone, false>(BwdParams);  \
   template __global__ void dkdv_kernel<E, 256, kMaskUpper, false>(BwdParams); \
   template __global__ void dkdv_kernel<E, 256, kMaskBand, false>(BwdParams);
@@ -1037,6 +1322,7 @@ FA_BWD_ALL(F16)
 #undef FA_BWD_SPLIT
 #undef FA_BWD_COMMON
 #undef FA_BWD_DQ
+#undef FA_BWD_DQPP
 
 template <typename E, int D, int MASK, bool BIAS>
 hipError_t launch(const BwdArgs& a) {
@@ -1097,16 +1383,24 @@ hipError_t launch(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (p.nqb > 0) {
-    // without a band, a ragged last key tile needs the masking variant
-    if constexpr (MASK == kMaskNone) {
-      if (g.nk % kTile != 0) {
-        hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, true>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0,
-                           a.stream, p);
-        return hipGetLastError();
-      }
+    if constexpr (!BIAS && D >= 96 && D <= 128) {
+      // two wave groups per work-group of 256 query rows (at d <= 64 the
+      // one-group kernel fits more waves per SIMD and was faster)
+      BwdParams pp = p;
+      pp.nqb = (g.nq + kDqpRows - 1) / kDqpRows;
+      const dim3 grid((unsigned)(pp.nqb * bh));
+      if (MASK == kMaskNone && g.nk % kTile != 0)
+        hipLaunchKernelGGL((dq_pp_kernel<E, D, MASK, MASK == kMaskNone>), grid, dim3(kDqpThreads), 0, a.stream, pp);
+      else
+        hipLaunchKernelGGL((dq_pp_kernel<E, D, MASK, false>), grid, dim3(kDqpThreads), 0, a.stream, pp);
+    } else if (MASK == kMaskNone && g.nk % kTile != 0) {
+      // without a band, a ragged last key tile needs the masking variant
+      hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, MASK == kMaskNone>), dim3((unsigned)(p.nqb * bh)),
+                         dim3(kThreads), 0, a.stream, p);
+    } else {
+      hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, false>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0,
+                         a.stream, p);
     }
-    hipLaunchKernelGGL((dq_kernel<E, D, MASK, BIAS, false>), dim3((unsigned)(p.nqb * bh)), dim3(kThreads), 0,
-                       a.stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
