@@ -11,6 +11,16 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    # FA_TEST_LIBRARY points the binding at another build of the library (the
+    # host-sanitized one); it must be loaded before any test module reads
+    # fa.LIB_PATH or calls fa.load_library().
+    alt = os.environ.get("FA_TEST_LIBRARY")
+    if alt:
+        from exact_attention_122_amd import fa
+        fa.LIB_PATH = alt
+        fa.load_library(alt)
+        sys.__stderr__.write(f"[library] {alt}\n")
+        sys.__stderr__.flush()
 
 
 def pytest_collection_modifyitems(config, items):
