@@ -206,12 +206,61 @@ __device__ __forceinline__ float max_tree(const float* x) {
   }
 }
 
+// Sum of N values as a pairwise tree: independent adds side by side.
+template <int N>
+__device__ __forceinline__ float sum_tree(const float* x) {
+  float t[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) t[i] = x[i] + x[i + N / 2];
+#pragma unroll
+  for (int w = N / 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] += t[i + w];
+  return t[0];
+}
+
+// S^T of the wave's tile once more, as the matrix phase formed it but with the
+// K rows read from global memory: by the time group B's softmax phase runs,
+// group A may already be copying the next tile into the LDS buffer.
+template <typename E, int D, int KB>
+__device__ __forceinline__ void recompute_scores(float (&x)[16 * KB], const bf16_t* kh, int k_sr, int key0, int nk,
+                                                 const bf16x8 (&qf)[D / 16], int lane) {
+  const int hw = lane >> 5, col = lane & 31;
+  f32x16 acc[KB];
+#pragma unroll
+  for (int b = 0; b < KB; ++b) acc[b] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const int kr = key0 + 32 * b + col;
+      u32x4 a = u32x4{0u, 0u, 0u, 0u};
+      if (kr < nk) a = *(const u32x4*)(kh + (long long)kr * k_sr + 16 * ks + 8 * hw);
+      acc[b] = E::mfma(__builtin_bit_cast(bf16x8, a), qf[ks], acc[b]);
+      // a rare path: one load at a time, so it takes no registers beyond
+      // what the rest of the kernel needs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[16 * b + r] = acc[b][r];
+}
+
 // Softmax phase for the tile whose scores are in st.s. With a bias the scores
 // become y = c s + log2(e) bias (log2 units) first; `masked` tiles (band
 // edges, ragged end) then set the scores of dead keys to -inf.
+//
+// Without a bias, once a row has a reference point the exponentials are taken
+// against it straight away, and the reference is checked afterwards, on the
+// sum of the lane's p: a sum of at most 2^8 bounds every p by 2^8, the bound
+// the max test below keeps. Only when a sum is larger (a score far above the
+// reference, or an overflow) are the scores formed again and the tile run
+// through the max path. That saves the max tree on nearly every tile.
 template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
-                                              bool masked, const float* brow, const f32x4 (&bpre)[4 * KB]) {
+                                              bool masked, const float* brow, const f32x4 (&bpre)[4 * KB],
+                                              const bf16_t* kh, const bf16x8 (&qf)[D / 16]) {
   constexpr int kN = 16 * KB;  // scores per lane
   const int hw = lane >> 5;
   // scale of the working units: raw scores without bias, log2 units with one
@@ -239,7 +288,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
         if (g == 3) __builtin_amdgcn_sched_barrier(0);
       }
   }
-  if (masked) {
+  auto mask_dead = [&](float (&y)[kN]) {
     // live keys of this row: [lo, hi]
     const int hi = MASK != kMaskNone ? min(qi + p.diag + p.wr, p.nk - 1) : p.nk - 1;
     const int lo = MASK == kMaskBand ? qi + p.diag - p.wl : 0;
@@ -248,45 +297,68 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
     for (int i = 0; i < kN; ++i) {
       const int b = i >> 4, r = i & 15;
       const int kr = k0 + 32 * b + 8 * (r >> 2) + (r & 3);
-      x[i] = (kr > hi || (MASK == kMaskBand && kr < lo)) ? -INFINITY : x[i];
+      y[i] = (kr > hi || (MASK == kMaskBand && kr < lo)) ? -INFINITY : y[i];
+    }
+  };
+  if (masked) mask_dead(x);
+
+  // moves the reference point to the tile's max where that grows by more
+  // than the threshold, rescaling O and l by the same factor
+  auto rebase = [&]() {
+    // Running max: in-lane as a tree, then across the half-wave pair. The
+    // softmax wave has its SIMD's vector ALU to itself during this phase, so
+    // only independent instructions hide each other's latency.
+    const float mx = pair_max(max_tree<kN>(x));
+    if (wave_any(!(mx <= st.m + thr))) {
+      const float mnew = fmaxf(st.m, mx);
+      const float ms = (mnew == -INFINITY) ? 0.f : mnew * cu;
+      const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m * cu - ms);
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) st.acc[db] *= alpha;
+      st.m = mnew;
+      st.mc = ms;
+    }
+  };
+  // p = exp2(c s - c m) and the lane's sum of p; c > 0, so dead keys
+  // (s = -inf) give exp2(-inf) = 0. FMAs, then exponentials, then a sum tree:
+  // independent instructions back to back instead of FMA -> exp -> add chains.
+  auto exponentials = [&]() {
+    const float nmc = -st.mc;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) x[i] = fmaf(x[i], cu, nmc);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) x[i] = fast_exp2(x[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    return sum_tree<kN>(x);
+  };
+
+  float ts;
+  if constexpr (BIAS) {
+    rebase();
+    ts = exponentials();
+  } else {
+    // a row without a reference point yet (no live key so far) takes the
+    // tile's max; its O and l are still zero, so nothing is rescaled
+    if (wave_any(st.m == -INFINITY)) {
+      const float mx = pair_max(max_tree<kN>(x));
+      if (st.m == -INFINITY) {
+        st.m = mx;
+        st.mc = (mx == -INFINITY) ? 0.f : mx * cu;
+      }
+    }
+    ts = exponentials();
+    if (wave_any(!(ts <= 256.f))) {
+      // rare: a score far above the reference point (or an overflow). The
+      // exponentials replaced the scores, so form them again.
+      recompute_scores<E, D, KB>(x, kh, p.k_sr, key0, p.nk, qf, lane);
+      if (masked) mask_dead(x);
+      rebase();
+      ts = exponentials();
     }
   }
-  // Running max: in-lane as a tree, then across the half-wave pair. The
-  // softmax wave has its SIMD's vector ALU to itself during this phase, so
-  // only independent instructions hide each other's latency.
-  const float mx = pair_max(max_tree<kN>(x));
-
-  if (wave_any(!(mx <= st.m + thr))) {
-    const float mnew = fmaxf(st.m, mx);
-    const float ms = (mnew == -INFINITY) ? 0.f : mnew * cu;
-    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m * cu - ms);
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.acc[db] *= alpha;
-    st.m = mnew;
-    st.mc = ms;
-  }
-
-  // p = exp2(c s - c m); c > 0, so dead keys (s = -inf) give exp2(-inf) = 0.
-  // FMAs, then exponentials, then a sum tree: independent instructions back
-  // to back instead of FMA -> exp -> add chains.
-  const float nmc = -st.mc;
-#pragma unroll
-  for (int i = 0; i < kN; ++i) x[i] = fmaf(x[i], cu, nmc);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < kN; ++i) x[i] = fast_exp2(x[i]);
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    float t[kN / 2];
-#pragma unroll
-    for (int i = 0; i < kN / 2; ++i) t[i] = x[i] + x[i + kN / 2];
-#pragma unroll
-    for (int w = kN / 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) t[i] += t[i + w];
-    st.l += t[0];
-  }
+  st.l += ts;
 #pragma unroll
   for (int t = 0; t < 2 * KB; ++t)
 #pragma unroll
@@ -312,7 +384,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const RowRead<D>& krd, const TrRead<D>& vrd,
                                               const bf16x8 (&qf)[D / 16], RowState<D, KB>& st, const FwdParams& p,
-                                              int wq0, int qi, int lane, const float* brow) {
+                                              int wq0, int qi, int lane, const float* brow, const bf16_t* kh) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
   // the bias of this tile, for the softmax phase after the matrix phase: read
@@ -340,7 +412,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
-  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow, bpre);
+  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow, bpre, kh, qf);
   if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
   if (!group_b) wait_vmem();
   lds_barrier();
@@ -353,8 +425,17 @@ constexpr int fwd_blocks_per_cu() {
   return D <= 64 ? 2 : 1;
 }
 
+// The waves each SIMD must hold (the second __launch_bounds__ argument, which
+// caps the registers per lane at 512 / that many): a work-group's 8 waves
+// spread over the 4 SIMDs of a CU. Kernels with a bias keep their tile's bias
+// in registers and run one work-group per CU.
+template <int D, bool BIAS>
+constexpr int fwd_waves_per_simd() {
+  return (BIAS ? 1 : fwd_blocks_per_cu<D>()) * kWaves / 4;
+}
+
 template <typename E, int D, int MASK, bool BIAS>
-__global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd_kernel(FwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
   constexpr int KB = key_blocks<D, BIAS>();
   constexpr int kBlockN = 32 * KB;  // keys per tile
@@ -445,13 +526,13 @@ __global__ __launch_bounds__(kThreads, fwd_blocks_per_cu<D>()) void fwd_kernel(F
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
     fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane, brow);
+                                  vrd, qf, st, p, wq0, qi, lane, brow, kh);
     fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs, vrs,
-                                  krd, vrd, qf, st, p, wq0, qi, lane, brow);
+                                  krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
   }
   if (j < n_tiles)
     fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane, brow);
+                                  vrd, qf, st, p, wq0, qi, lane, brow, kh);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
   pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) lds_barrier();

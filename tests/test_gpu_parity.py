@@ -126,6 +126,35 @@ def test_fwd_adversarial_rescale(kind, causal):
     compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
 
 
+@pytest.mark.parametrize("kind", ["overflow", "jump", "crowd"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_fwd_reference_point_fallback(kind, causal, d):
+    """Tiles whose exponentials, taken against the row's current reference
+    point, sum to more than 2^8 per lane, so the kernel forms the scores again
+    and moves the reference: a key whose score is hundreds of log2 units above
+    the earlier ones (the first exponentials overflow to inf), a jump of about
+    40 units, and a crowd of 64 keys each about 5 units above the reference
+    (a large sum while the max stays under the rescale threshold)."""
+    n = 333
+    rng = np.random.Generator(np.random.PCG64(4600 + d))
+    scale = inputs.default_scale(d)
+    q = 1.0 + 0.1 * rng.standard_normal((1, 2, n, d), dtype=np.float32)
+    k = 0.1 * rng.standard_normal((1, 2, n, d), dtype=np.float32)
+    v = rng.standard_normal((1, 2, n, d), dtype=np.float32)
+    if kind == "overflow":
+        k[:, :, 150, :] = 20.0
+    elif kind == "jump":
+        k[:, :, 150, :] = 30.0 / (d * scale)
+    else:
+        k[:, :, 200:264, :] = 3.5 / (d * scale)
+    g = {name: inputs.Tensor(inputs.f32_to_bf16_bits(x), "bf16") for name, x in zip("qkv", (q, k, v))}
+    _, _, _, o, lse = gpu_fwd(g, causal, scale)
+    ro, rl = _oracle_fwd(g, scale, causal)
+    compare("O", f64(o), ro, TOL["bf16"]["o"], REL_FRO)
+    compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
+
+
 def test_constant_v_and_identical_keys_on_gpu():
     n, d = 256, 64
     rng = np.random.Generator(np.random.PCG64(4600))
