@@ -673,7 +673,7 @@ __device__ __forceinline__ void pp_run(int t_begin, int t_end, const PpBufs& b0,
 }
 
 template <typename E, int D, int MASK>
-__global__ __launch_bounds__(kPpThreads, 1) void dkdv_pp_kernel(BwdParams p) {
+__global__ __launch_bounds__(kPpThreads, 2) void dkdv_pp_kernel(BwdParams p) {
   constexpr int P = lds_pitch<D>();
   __shared__ __attribute__((aligned(1024))) bf16_t q_lds0[kTile * P];
   __shared__ __attribute__((aligned(1024))) bf16_t q_lds1[kTile * P];
@@ -1151,7 +1151,7 @@ __device__ __forceinline__ void dqp_iteration(int j, int n_tiles, int key_base, 
 }
 
 template <typename E, int D, int MASK, bool RAGGED>
-__global__ __launch_bounds__(kDqpThreads, 1) void dq_pp_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDqpThreads, 2) void dq_pp_kernel(BwdParams p) {
   constexpr bool BAND = MASK != kMaskNone;
   constexpr bool MASK_CODE = BAND || RAGGED;
   constexpr int P = lds_pitch<D>();

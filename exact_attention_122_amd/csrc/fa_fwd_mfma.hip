@@ -253,10 +253,16 @@ __device__ __forceinline__ void recompute_scores(float (&x)[16 * KB], const bf16
 //
 // Without a bias, once a row has a reference point the exponentials are taken
 // against it straight away, and the reference is checked afterwards, on the
-// sum of the lane's p: a sum of at most 2^8 bounds every p by 2^8, the bound
-// the max test below keeps. Only when a sum is larger (a score far above the
-// reference, or an overflow) are the scores formed again and the tile run
-// through the max path. That saves the max tree on nearly every tile.
+// sum of the lane's p: a sum of at most kFastSumBound bounds every p by it.
+// fp32 has ample room for p that large (O / l and m + ln l do not depend on
+// the reference point; the max test below moves it at a factor 2^8 only to
+// move it rarely). Only a larger sum (a score far above the reference, or an
+// overflow) has the scores formed again and the tile run through the max
+// path. That saves the max tree on nearly every tile. The bound is set well
+// above 2^8 because a row's first reference can come from a tile with only a
+// few live keys (a band edge), and ordinary later tiles then sum to a few
+// hundred.
+constexpr float kFastSumBound = 65536.f;
 template <typename E, int D, int KB, int MASK, bool BIAS>
 __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdParams& p, int key0, int qi, int lane,
                                               bool masked, const float* brow, const f32x4 (&bpre)[4 * KB],
@@ -349,7 +355,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
       }
     }
     ts = exponentials();
-    if (wave_any(!(ts <= 256.f))) {
+    if (wave_any(!(ts <= kFastSumBound))) {
       // rare: a score far above the reference point (or an overflow). The
       // exponentials replaced the scores, so form them again.
       recompute_scores<E, D, KB>(x, kh, p.k_sr, key0, p.nk, qf, lane);

@@ -126,16 +126,17 @@ def test_fwd_adversarial_rescale(kind, causal):
     compare("LSE", f64(lse), rl, TOL["bf16"]["lse"])
 
 
-@pytest.mark.parametrize("kind", ["overflow", "jump", "crowd"])
+@pytest.mark.parametrize("kind", ["overflow", "jump", "rise", "crowd"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_fwd_reference_point_fallback(kind, causal, d):
-    """Tiles whose exponentials, taken against the row's current reference
-    point, sum to more than 2^8 per lane, so the kernel forms the scores again
-    and moves the reference: a key whose score is hundreds of log2 units above
-    the earlier ones (the first exponentials overflow to inf), a jump of about
-    40 units, and a crowd of 64 keys each about 5 units above the reference
-    (a large sum while the max stays under the rescale threshold)."""
+    """Tiles far above a row's reference point. The kernel takes the
+    exponentials against the current reference first and checks their lane
+    sum; past 2^16 it forms the scores again and moves the reference. Cases: a
+    key hundreds of log2 units above the earlier ones (the first exponentials
+    overflow to inf) and a jump of about 40 units, both through the fallback; a
+    rise of about 12 units and a crowd of 64 keys about 5 units up, both kept
+    against the old reference (p up to 2^12 and large sums)."""
     n = 333
     rng = np.random.Generator(np.random.PCG64(4600 + d))
     scale = inputs.default_scale(d)
@@ -146,6 +147,8 @@ def test_fwd_reference_point_fallback(kind, causal, d):
         k[:, :, 150, :] = 20.0
     elif kind == "jump":
         k[:, :, 150, :] = 30.0 / (d * scale)
+    elif kind == "rise":
+        k[:, :, 150, :] = 8.5 / (d * scale)
     else:
         k[:, :, 200:264, :] = 3.5 / (d * scale)
     g = {name: inputs.Tensor(inputs.f32_to_bf16_bits(x), "bf16") for name, x in zip("qkv", (q, k, v))}
