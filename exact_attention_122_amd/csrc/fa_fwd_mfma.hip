@@ -23,13 +23,15 @@
 //    kept together as one set, double-buffered in LDS, and copied global ->
 //    LDS with buffer_load ... lds (zero-fill past the end). The copies are
 //    split between the groups: group A copies K_{j+1} at the start of its
-//    matrix phase j; group B copies V_{j+1} into set j's buffer (set j + 2)
-//    at the end of its softmax phase j, once both groups have read set j and
-//    once group A's K copy of the same phase has drained (issued at the start
-//    of the phase, behind that copy, the V copy stalled group B's softmax by
-//    about a third). Each copy has a whole phase after its issue to land:
-//    the barriers wait only for LDS accesses (lds_barrier), and each group
-//    waits for its own copy just before the barrier that hands it over.
+//    matrix phase j (of its softmax phase j at d = 256, whose short phases
+//    carry the copy's issue less well); group B copies V_{j+1} into set j's
+//    buffer (set j + 2) at the end of its softmax phase j, once both groups
+//    have read set j and once group A's K copy of the same phase has drained
+//    (issued at the start of the phase, behind that copy, the V copy stalled
+//    group B's softmax by about a third). Each copy has at least a whole
+//    phase after its issue to land: the barriers wait only for LDS accesses
+//    (lds_barrier), and each group waits for its own copy just before the
+//    barrier that hands it over.
 //  * Scores are computed transposed, S^T = K Q^T, with Q (the B operand) kept
 //    in registers. Each lane then holds one query's scores for 32 keys, so the
 //    row max and row sum are in-lane reductions plus one exchange across the
@@ -404,15 +406,21 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
 #pragma unroll
       for (int g = 0; g < 4; ++g) bpre[4 * b + g] = load_bias4(brow, key0 + 32 * b + 8 * g + 4 * hw, p.nk);
   }
-  // group A copies K_{j+1} into set j + 1 during its matrix phase and waits
-  // for it at the end of its softmax phase; group B copies V_{j+1} into set
-  // j's buffer (which becomes set j + 2) at the end of its softmax phase,
-  // once both groups have read set j, and waits for it at the end of its next
-  // matrix phase
-  if (!group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
+  // group A copies K_{j+1} into set j + 1 during its matrix phase (softmax
+  // phase at d = 256) and waits for it at the end of its softmax phase; group
+  // B copies V_{j+1} into set j's buffer (which becomes set j + 2) at the end
+  // of its softmax phase, once both groups have read set j, and waits for it
+  // at the end of its next matrix phase.
+  // At d = 256 (32-key tiles, short phases) group A issues the copy at the
+  // start of its softmax phase instead, where it weighs less on the critical
+  // matrix phase; the copy then has one phase to land instead of two. That
+  // was 2 % faster at d = 256 and 1-3 % slower at d = 96 and 128.
+  constexpr bool kLateK = D >= 256;
+  if (!kLateK && !group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
   matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
   if (group_b) wait_vmem();
   lds_barrier();
+  if (kLateK && !group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
   // the wave's rows are wq0 .. wq0 + 31: the last has the highest lower
   // bound, the first the lowest upper bound
   const bool masked = (key0 + kBlockN > p.nk) ||
