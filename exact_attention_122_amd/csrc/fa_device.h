@@ -261,15 +261,18 @@ struct TileDma {
   // bytes apart) into `tile`. The whole offset goes in the vector offset: the
   // buffer range check that zero-fills rows past the end does not include the
   // scalar offset.
-  // The stride is laundered through an empty asm so the compiler computes
-  // the offsets here, per copy, instead of hoisting kInstr loop-invariant
-  // offsets per tensor into registers for the whole loop.
+  // The stride and the LDS destination are laundered through empty asm so the
+  // compiler computes the offsets and the kInstr destination addresses here,
+  // per copy, instead of hoisting them per tensor and per buffer into
+  // registers for the whole loop.
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0, uint32_t stride) const {
     asm volatile("" : "+s"(stride));
     const uint32_t lane_base = (lrow + (uint32_t)row0) * stride;
+    uint32_t dst0 = (uint32_t)(uintptr_t)((FA_LDS char*)(FA_LDS bf16_t*)tile + lds_off);
+    asm volatile("" : "+s"(dst0));
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
-      FA_LDS void* dst = (FA_LDS void*)((FA_LDS char*)(FA_LDS bf16_t*)tile + lds_off + i * 1024);
+      FA_LDS void* dst = (FA_LDS void*)(uintptr_t)(dst0 + i * 1024);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, lane_base + chunk_off[i % kPeriod] + i * kRowsPerInstr * stride, 0,
                                                0, 0);
     }
