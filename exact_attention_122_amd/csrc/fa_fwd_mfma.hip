@@ -157,8 +157,11 @@ __device__ __forceinline__ void matrix_phase(RowState<D, KB>& st, const bf16_t* 
     fence_regs(st.s[b]);
   }
   // PV: (D / 32) (2 KB) MFMAs, two transposed reads each; S: KB (D / 16)
-  // MFMAs, one read each
-  constexpr int kPv = D * KB / 16, kS = KB * D / 16, kAhead = 4;
+  // MFMAs, one read each. At d = 64 (128 registers per lane) and d = 256
+  // (128 of the 256 registers hold O) four operands in flight push the phase
+  // past the register budget, and the scheduler then drops the pattern
+  // altogether (every MFMA waits for its own read); two fit.
+  constexpr int kPv = D * KB / 16, kS = KB * D / 16, kAhead = (D == 64 || D == 256) ? 2 : 4;
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAhead, 0);
 #pragma unroll
   for (int i = 0; i < kPv - kAhead; ++i) {
