@@ -154,6 +154,21 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const bf16_t* o, co
   }
 }
 
+// Scheduling groups (see __builtin_amdgcn_sched_group_barrier) for a block of
+// N MFMAs that each take R LDS reads: the operands of A MFMAs are read ahead
+// of the MFMA that issues, so the matrix core does not wait on LDS latency.
+template <int N, int R, int A>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);
+#pragma unroll
+  for (int i = 0; i < N - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < A; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
 // ---------------------------------------------------------------- dK, dV ---
 
 // One 64-query tile against the wave's 32 keys. With a band, `masked` tiles
@@ -812,6 +827,9 @@ __device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, cons
       dpt[kb] = E::mfma(rrd(vt, kb, ks), df[ks], dpt[kb]);
     }
   }
+  // two operands in flight: without a pattern every MFMA waited for its own
+  // read (at d = 256 all 192 of them)
+  sched_reads_ahead<4 * (D / 16), 1, 2>();
   bf16x8 ds[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -849,6 +867,7 @@ __device__ __forceinline__ void dq_tile(const bf16_t* kt, const bf16_t* vt, cons
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int t = 0; t < 4; ++t) dq[db] = E::mfma(trd(kt, t, db), ds[t], dq[db]);
+  sched_reads_ahead<4 * (D / 32), 2, 2>();
 }
 
 template <typename E, int D, int MASK, bool BIAS, bool MASK_CODE>
