@@ -1055,6 +1055,12 @@ struct DqpState {
   float lse2, drow;
 };
 
+// Operands in flight in the dQ kernel's matrix phase: three, where four
+// pushed the causal kernel at d = 128 to 256 registers and the scheduler then
+// dropped part of the pattern (43 of 240 MFMAs waited on their own read, 14
+// with three).
+constexpr int kDqpAhead = 3;
+
 template <typename E, int D>
 __device__ __forceinline__ void dqp_matrix(DqpState<D>& st, const bf16_t* kprev, const bf16_t* kcur,
                                            const bf16_t* vcur, bool prev, bool cur, const RowRead<D>& rrd,
@@ -1065,14 +1071,14 @@ __device__ __forceinline__ void dqp_matrix(DqpState<D>& st, const bf16_t* kprev,
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) st.dq[db] = E::mfma(trd(kprev, t, db), st.ds[t], st.dq[db]);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPpAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kDqpAhead, 0);
 #pragma unroll
-    for (int i = 0; i < kN - kPpAhead; ++i) {
+    for (int i = 0; i < kN - kDqpAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    for (int i = 0; i < kDqpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
   }
   if (cur) {
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -1092,14 +1098,14 @@ __device__ __forceinline__ void dqp_matrix(DqpState<D>& st, const bf16_t* kprev,
     }
     // one row read per MFMA
     constexpr int kR = D / 4;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPpAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDqpAhead, 0);
 #pragma unroll
-    for (int i = 0; i < kR - kPpAhead; ++i) {
+    for (int i = 0; i < kR - kDqpAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kPpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    for (int i = 0; i < kDqpAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
   }
 }
 
