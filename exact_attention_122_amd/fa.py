@@ -42,6 +42,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is not built: run `python -m exact_attention_122_amd.build` "
             "(or __graft_entry__.build()); there is no other implementation to fall back on")
+    # torch ships its own HIP runtime. Loaded first, it is the one libfa.so
+    # binds to; loaded after libfa.so, a second runtime would come in beside
+    # the system one, and the library's launches would find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_version.restype = i
