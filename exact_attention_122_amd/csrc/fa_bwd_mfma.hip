@@ -180,7 +180,7 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
                                           const RowRead<D>& rrd, const TrRead<D>& trd, const bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
                                           float c, int q0, int q_lo, int q_hi, int lane, bool masked,
-                                          const float* bcol, long long bias_sr, int nq) {
+                                          const float* bcol, bool bkey, long long bias_sr, int nq) {
   const int hw = lane >> 5;
   // The tile's bias down this lane's key column, read before the S/dP
   // products so that its latency hides behind them (read next to its use, it
@@ -190,7 +190,9 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int qr = q0 + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * hw + (i & 3);
-      bpre[i] = (bcol && qr < nq) ? bcol[qr * bias_sr] : 0.f;
+      // every lane loads (row and column clamped into the bias): no branch
+      // per load; rows or keys past the end are zeroed where the value is used
+      bpre[i] = bcol[(long long)min(qr, nq - 1) * bias_sr];
     }
   }
   f32x16 s[2], dp[2];
@@ -219,12 +221,14 @@ __device__ __forceinline__ void dkdv_tile(const bf16_t* qt, const bf16_t* dt, co
         const int i = 4 * g + rr;
         float arg = fmaf(s[qb][i], c, -Lv[rr]);
         if constexpr (BIAS) {
-          // bias[q][key] down this lane's key column (bcol is null past the last key)
+          // bias[q][key] down this lane's key column (bkey: the key exists)
           if constexpr (D <= 128) {
-            arg = fmaf(kLog2e, bpre[qb * 16 + i], arg);
+            const int qr = q0 + r0 + rr;
+            arg = fmaf(kLog2e, (bkey && qr < nq) ? bpre[qb * 16 + i] : 0.f, arg);
           } else {
             const int qr = q0 + r0 + rr;
-            if (bcol && qr < nq) arg = fmaf(kLog2e, bcol[qr * bias_sr], arg);
+            const float bv = bcol[(long long)min(qr, nq - 1) * bias_sr];
+            if (bkey && qr < nq) arg = fmaf(kLog2e, bv, arg);
           }
         }
         if (MASK != kMaskNone && masked) {
@@ -278,7 +282,7 @@ __device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur
                                             const DkdvCopy<D>& cp, const RowRead<D>& rrd, const TrRead<D>& trd,
                                             const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                             f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const BwdParams& p,
-                                            int wk0, int q_lo, int q_hi, int lane, const float* bcol) {
+                                            int wk0, int q_lo, int q_hi, int lane, const float* bcol, bool bkey) {
   const int q0 = t * kTile;
   if (t + 1 < t_end) cp.issue(nxt, q0 + kTile);
   bool live = wk0 < p.nk, masked = false;
@@ -291,7 +295,7 @@ __device__ __forceinline__ void dkdv_step(int t, int t_end, const QTileBufs& cur
     }
   }
   if (live)
-    dkdv_tile<E, D, MASK, BIAS>(cur.q, cur.d, cur.st, rrd, trd, kf, vf, dk, dv, p.c, q0, q_lo, q_hi, lane, masked, bcol,
+    dkdv_tile<E, D, MASK, BIAS>(cur.q, cur.d, cur.st, rrd, trd, kf, vf, dk, dv, p.c, q0, q_lo, q_hi, lane, masked, bcol, bkey,
                                 p.bias_sr, p.nq);
   wait_vmem();
   __syncthreads();
@@ -322,11 +326,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   const int key = wk0 + col;
   // query rows that see this lane's key: [key - diag - wr, key - diag + wl]
   const int q_lo = key - p.diag - p.wr, q_hi = key - p.diag + p.wl;
-  // this lane's bias column (null past the last key)
+  // this lane's bias column (the last key's past the end, where bkey is
+  // false and the values read are not used)
   const float* bcol = nullptr;
-  if (BIAS && key < nk) {
+  const bool bkey = key < nk;
+  if (BIAS) {
     const int b = head / p.heads;
-    bcol = p.bias + b * p.bias_sb + (head - b * p.heads) * p.bias_sh + key;
+    bcol = p.bias + b * p.bias_sb + (head - b * p.heads) * p.bias_sh + min(key, nk - 1);
   }
 
   // query tiles of this work-group's band
@@ -379,9 +385,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
   for (int t = t_begin; t < t_end; t += 2) {
-    dkdv_step<E, D, MASK, BIAS>(t, t_end, b0, b1, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol);
+    dkdv_step<E, D, MASK, BIAS>(t, t_end, b0, b1, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol, bkey);
     if (t + 1 < t_end)
-      dkdv_step<E, D, MASK, BIAS>(t + 1, t_end, b1, b0, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol);
+      dkdv_step<E, D, MASK, BIAS>(t + 1, t_end, b1, b0, cp, rrd, trd, kf, vf, dk, dv, p, wk0, q_lo, q_hi, lane, bcol, bkey);
   }
 
   // lane holds d = 32 db + col for keys wk0 + 8 g + 4 hw + rr
