@@ -492,9 +492,9 @@ struct PpState {
 // whether the wave's keys see the previous and the current tile.
 // Scheduling groups (see __builtin_amdgcn_sched_group_barrier): instruction
 // classes the compiler's scheduler must place in the given order. Each block
-// of products keeps kPpAhead LDS operands in flight ahead of its MFMAs;
-// unconstrained, the scheduler issues every read of the block first and runs
-// out of registers.
+// of products in the dK/dV kernel keeps kPpAhead LDS operands in flight ahead
+// of its MFMAs (the dQ kernel's count is kDqpAhead); unconstrained, the
+// scheduler issues every read of the block first and runs out of registers.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kPpAhead = 4;
