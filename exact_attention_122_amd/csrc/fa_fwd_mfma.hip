@@ -540,16 +540,34 @@ __global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd
   // read by group B in phase 2j + 1, and set j + 1 is first read by group A in
   // phase 2j + 2.
   if (group_b) lds_barrier();
+  // Tiles run in pairs (set 0, then set 1). At d = 64 and 256, whose
+  // registers are tightest, an odd last tile runs the first half of a pair
+  // inside the loop, and the epilogue forms its lane values again: no tail
+  // copy of the iteration follows the loop, and nothing computed before the
+  // loop has to survive it (that had cost 1-6 spilled registers and, at
+  // d = 256, most of the matrix phase's operand read-ahead). Elsewhere the
+  // odd tile runs after the loop, which measured slightly faster.
+  constexpr bool kCompact = D == 64 || D == 256;
   int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
-    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane, brow, kh);
-    fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs, vrs,
-                                  krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+  if constexpr (kCompact) {
+    for (; j < n_tiles; j += 2) {
+      fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
+                                    vrd, qf, st, p, wq0, qi, lane, brow, kh);
+      if (j + 1 < n_tiles)
+        fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs,
+                                      vrs, krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+    }
+  } else {
+    for (; j + 1 < n_tiles; j += 2) {
+      fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
+                                    vrd, qf, st, p, wq0, qi, lane, brow, kh);
+      fwd_iteration<E, D, KB, MASK, BIAS>(j + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs, vrs,
+                                    krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+    }
+    if (j < n_tiles)
+      fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
+                                    vrd, qf, st, p, wq0, qi, lane, brow, kh);
   }
-  if (j < n_tiles)
-    fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
-                                  vrd, qf, st, p, wq0, qi, lane, brow, kh);
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
   pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) lds_barrier();
@@ -557,6 +575,17 @@ __global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd
   // epilogue: O = acc / l, LSE = m * |scale| + ln l (-inf for a row with no key)
   const float lt = pair_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // (kCompact: the row and half-wave are formed again from the thread index,
+  // laundered so the compiler cannot carry the values from before the loop)
+  int qi_e = qi, hw_e = hw;
+  if constexpr (kCompact) {
+    int te = tid;
+    asm volatile("" : "+v"(te));
+    qi_e = q_row0 + (te >> 6) * 32 + (te & 31);
+    hw_e = (te >> 5) & 1;
+  }
+  {
+    const int qi = qi_e, hw = hw_e;
   if (qi < nq) {
     bf16_t* orow = p.o + hb * p.o_sb + hh * p.o_sh + (long long)qi * p.o_sr;
 #pragma unroll
@@ -572,6 +601,7 @@ __global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd
     // bias, in log2 units (scale ln 2)
     const float unit = BIAS ? kLn2 : p.scale_abs;
     if (hw == 0) p.lse[(long long)head * nq + qi] = lt > 0.f ? st.m * unit + __logf(lt) : -INFINITY;
+  }
   }
 }
 
