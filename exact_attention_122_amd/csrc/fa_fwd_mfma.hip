@@ -61,6 +61,8 @@
 //    consecutive keys per 16-byte load, at the start of the matrix phase that
 //    precedes the softmax phase using it (64-key tiles make room for it in
 //    the registers), so the load latency hides behind the MFMAs.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -387,7 +389,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 // can see that reading set j never depends on a copy into the other set. Every
 // wave runs every tile of its work-group: a tile wholly outside a wave's band
 // has all scores at -inf, so its p are 0 and it changes nothing.
-template <typename E, int D, int KB, int MASK, bool BIAS>
+template <typename E, int D, int KB, int MASK, bool BIAS, bool FULL = true>
 __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, bool group_b, const bf16_t* kt,
                                               bf16_t* vt,
                                               bf16_t* kn,
@@ -402,7 +404,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   // now, so its latency hides behind the matrix phase (and ahead of the tile
   // copy, so waiting for it never waits for the copy)
   f32x4 bpre[4 * KB];
-  if constexpr (bias_ahead<D, BIAS>()) {
+  if constexpr (FULL && bias_ahead<D, BIAS>()) {
     const int hw = lane >> 5;
 #pragma unroll
     for (int b = 0; b < KB; ++b)
@@ -420,7 +422,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   // was 2 % faster at d = 256 and 1-3 % slower at d = 96 and 128.
   constexpr bool kLateK = D >= 256;
   if (!kLateK && !group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
-  matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
+  if constexpr (FULL) matrix_phase<E, D, KB>(st, kt, vt, krd, vrd, qf);
   if (group_b) wait_vmem();
   lds_barrier();
   if (kLateK && !group_b && j + 1 < n_tiles) dma.issue(krs, kn, key0 + kBlockN, 2u * p.k_sr);
@@ -429,7 +431,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
   const bool masked = (key0 + kBlockN > p.nk) ||
                       (MASK != kMaskNone && key0 + kBlockN - 1 > wq0 + p.diag + p.wr) ||
                       (MASK == kMaskBand && key0 < wq0 + 31 + p.diag - p.wl);
-  softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow, bpre, kh, qf);
+  if constexpr (FULL) softmax_phase<E, D, KB, MASK, BIAS>(st, p, key0, qi, lane, masked, brow, bpre, kh, qf);
   if (group_b && j + 1 < n_tiles) dma.issue(vrs, vt, key0 + kBlockN, 2u * p.v_sr);
   if (!group_b) wait_vmem();
   lds_barrier();
@@ -549,7 +551,50 @@ __global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd
   // odd tile runs after the loop, which measured slightly faster.
   constexpr bool kCompact = D == 64 || D == 256;
   int j = 0;
-  if constexpr (kCompact) {
+  // (band kernels: the pending P V of the last live tile is done in the tile
+  // after it, or after the loop when that is the last tile)
+  bool last_pv = true;
+  if constexpr (MASK == kMaskBand && D <= 128) {
+    // Each wave runs the tiles its own rows see, [ja, je), in full; the tiles
+    // before and after them only issue their share of the copies and take
+    // part in the barriers. A tile none of its rows sees would change
+    // nothing (all its scores -inf); leaving its MFMAs and exponentials out
+    // saves energy, which the power-limited clock turns into time (d = 256,
+    // which has no registers for the extra loop copies, runs every tile). je - 1 is
+    // the tile after the last live one: its matrix phase adds the last live
+    // tile's P V, and its own scores are all masked.
+    const int klo = max(wq0 + p.diag - p.wl, 0), khi = min(wq0 + 31 + p.diag + p.wr, nk - 1);
+    int ja = n_tiles, je = n_tiles;
+    if (klo <= khi && wq0 < nq) {
+      ja = klo < key_base ? 0 : min((klo - key_base) / kBlockN, n_tiles);
+      je = khi < key_base ? 0 : min((khi - key_base) / kBlockN + 2, n_tiles);
+      ja = __builtin_amdgcn_readfirstlane(ja);
+      je = __builtin_amdgcn_readfirstlane(max(je, ja));
+    }
+    last_pv = je == n_tiles && ja < je;
+    // tiles [a, b) of one kind, each on LDS set j % 2
+    auto run = [&](auto full, int a, int b) __attribute__((always_inline)) {
+      constexpr bool F = decltype(full)::value;
+      int i = a;
+      if (i < b && (i & 1)) {
+        fwd_iteration<E, D, KB, MASK, BIAS, F>(i, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs, vrs,
+                                              krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+        ++i;
+      }
+      for (; i + 1 < b; i += 2) {
+        fwd_iteration<E, D, KB, MASK, BIAS, F>(i, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs,
+                                              krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+        fwd_iteration<E, D, KB, MASK, BIAS, F>(i + 1, n_tiles, key_base, group_b, k_lds1, v_lds1, k_lds0, dma, krs,
+                                              vrs, krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+      }
+      if (i < b)
+        fwd_iteration<E, D, KB, MASK, BIAS, F>(i, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs,
+                                              krd, vrd, qf, st, p, wq0, qi, lane, brow, kh);
+    };
+    run(std::false_type{}, 0, ja);
+    run(std::true_type{}, ja, je);
+    run(std::false_type{}, je, n_tiles);
+  } else if constexpr (kCompact) {
     for (; j < n_tiles; j += 2) {
       fwd_iteration<E, D, KB, MASK, BIAS>(j, n_tiles, key_base, group_b, k_lds0, v_lds0, k_lds1, dma, krs, vrs, krd,
                                     vrd, qf, st, p, wq0, qi, lane, brow, kh);
@@ -569,7 +614,7 @@ __global__ __launch_bounds__(kThreads, (fwd_waves_per_simd<D, BIAS>())) void fwd
                                     vrd, qf, st, p, wq0, qi, lane, brow, kh);
   }
   // last tile: O += P V of set n_tiles (no copy is in flight any more)
-  pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
+  if (last_pv) pv_mfma<E, D, KB>(st, (n_tiles & 1) ? v_lds1 : v_lds0, vrd);
   if (!group_b) lds_barrier();
 
   // epilogue: O = acc / l, LSE = m * |scale| + ln l (-inf for a row with no key)
