@@ -389,6 +389,27 @@ __device__ __forceinline__ void softmax_phase(RowState<D, KB>& st, const FwdPara
 // can see that reading set j never depends on a copy into the other set. Every
 // wave runs every tile of its work-group: a tile wholly outside a wave's band
 // has all scores at -inf, so its p are 0 and it changes nothing.
+// Two work-groups share a CU at d = 64, and the issue arbiter favours the
+// older one's waves: one would finish in about two thirds of the other's
+// time and leave the CU half idle. Each wave lowers its priority as its
+// work-group gets through its tiles, so the one behind wins arbitration
+// (priority 3, 2, 1, 0 over the four quarters of its tiles). At d = 32 the
+// dispatcher's backfilling over many rounds already evens this out.
+template <int D, int MASK>
+__device__ __forceinline__ void progress_priority(int j, int n_tiles) {
+  if constexpr (D == 64 && MASK == kMaskNone) {
+    if (j == 0) {
+      __builtin_amdgcn_s_setprio(3);
+    } else if (4 * j == n_tiles || 4 * j == n_tiles + 1 || 4 * j == n_tiles + 2 || 4 * j == n_tiles + 3) {
+      __builtin_amdgcn_s_setprio(2);
+    } else if (2 * j == n_tiles || 2 * j == n_tiles + 1) {
+      __builtin_amdgcn_s_setprio(1);
+    } else if (4 * j == 3 * n_tiles || 4 * j == 3 * n_tiles + 1 || 4 * j == 3 * n_tiles + 2 || 4 * j == 3 * n_tiles + 3) {
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+}
+
 template <typename E, int D, int KB, int MASK, bool BIAS, bool FULL = true>
 __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, bool group_b, const bf16_t* kt,
                                               bf16_t* vt,
@@ -400,6 +421,7 @@ __device__ __forceinline__ void fwd_iteration(int j, int n_tiles, int key_base, 
                                               int wq0, int qi, int lane, const float* brow, const bf16_t* kh) {
   constexpr int kBlockN = 32 * KB;
   const int key0 = key_base + j * kBlockN;
+  progress_priority<D, MASK>(j, n_tiles);
   // the bias of this tile, for the softmax phase after the matrix phase: read
   // now, so its latency hides behind the matrix phase (and ahead of the tile
   // copy, so waiting for it never waits for the copy)
